@@ -1,0 +1,7 @@
+"""CPU oracle for the routed MoE FFN -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow numpy evaluation of what the HIP library computes, used by the
+tests, by the smoke check and by the CPU-baseline leg of the benchmark.  The
+product path never imports it.  See ``oracle/moe_oracle.py``.
+"""
+from .moe_oracle import *  # noqa: F401,F403
