@@ -1,0 +1,178 @@
+/*
+ * moe_ffn.h -- C ABI of the routed mixture-of-experts FFN library (gfx950).
+ *
+ * The library computes one routed MoE FFN layer of a large sparse LLM: a
+ * linear router picks the top-k of E experts per token, each chosen expert is
+ * a SwiGLU FFN whose weights are stored in 2- or 3-bit block quantisation, and
+ * the layer output is the gate-weighted sum of the k expert outputs.
+ *
+ * Sources: the Strata write-ups describe a model with 24,576 experts of which
+ * each token uses 10 (aiproducthub "Strata Skill", section 介绍; bnskd "Strata：
+ * 把 125B 大模型塞进 12GB 显卡", section 核心思路), 512 experts per layer over 48
+ * layers (yudady notes "Strata — 8~12GB 显存跑 125B", section 5 table; bnskd,
+ * section 投机解码), experts served from 2-bit "Q2_0" weights (aiproducthub,
+ * section 功能与原则) and prefill processed in chunks of up to 8,192 tokens
+ * (bnskd, section 工程细节).  The pages give no kernel interface; the calls
+ * below follow that problem statement.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ * - Pointers marked "device" must point to device memory of the current HIP
+ *   device.  The caller owns every buffer; the library allocates and frees
+ *   nothing and keeps nothing between calls except what the caller hands in.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues asynchronous work on it; outputs are valid once the stream has
+ *   reached that point.  Nothing synchronises.
+ * - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Arguments are
+ *   validated before anything is launched; on an error nothing is enqueued
+ *   (except MOE_ERR_HIP, reported when a launch itself fails).  Nothing throws.
+ * - Workspaces: `ws` is device scratch of at least moe_workspace_size(...)
+ *   bytes, 256-byte aligned.  It must be zero-filled once before its first
+ *   use; every call leaves the counters it uses at zero again, so one zeroed
+ *   workspace serves any number of calls.  Calls that run concurrently need
+ *   distinct workspaces.
+ * - Inputs are assumed finite; NaN logits give unspecified routing.
+ *
+ * Stored expert weights
+ * ---------------------
+ * Each matrix applied as x @ W with W of shape [K x N] is stored output-major:
+ * row n holds its K reduction weights in blocks of 32 consecutive k.
+ *   codes  uint32 [E][N][K/32][words]   words = 2 (2-bit) or 3 (3-bit)
+ *   scales uint16 [E][N][K/32]          IEEE binary16 bit patterns
+ * gate and up use K = d_model, N = d_ff; down uses K = d_ff, N = d_model.
+ * 2-bit: code = level + 2 (levels -2..1), weight i of a block in word i/16 at
+ * bits [2(i mod 16), +2).  3-bit: code = level + 4 (levels -4..3), the three
+ * words are one little-endian 96-bit string, weight i at bits [3i, 3i+3).
+ * Dequantised weight = level * scale (exact in fp32).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK               0
+#define MOE_ERR_ARG         -1  /* null pointer, non-positive size, bad dtype       */
+#define MOE_ERR_UNSUPPORTED -2  /* shape/format outside what the kernels handle     */
+#define MOE_ERR_WORKSPACE   -3  /* workspace missing, too small or misaligned       */
+#define MOE_ERR_NO_DEVICE   -4  /* no HIP device, or the device is not gfx950       */
+#define MOE_ERR_HIP         -5  /* a kernel launch failed (hipGetLastError)         */
+
+/* activation dtypes */
+#define MOE_F32  0
+#define MOE_BF16 1
+
+/* operations for moe_workspace_size */
+#define MOE_OP_ROUTE   0
+#define MOE_OP_DECODE  1
+#define MOE_OP_PREFILL 2
+
+/* Linear router of one layer.
+ *   w    device fp32 [d_model][n_experts] row-major
+ *   bias device fp32 [n_experts], or NULL for no bias
+ * Supported: d_model multiple of 32 and <= 16384, 1 <= top_k <= min(n_experts, 64),
+ * n_experts <= 1024. */
+typedef struct {
+    int d_model;
+    int n_experts;
+    int top_k;
+    const float* w;
+    const float* bias;
+} moe_router_t;
+
+/* Stored experts of one layer (layout above).  All pointers device.
+ * Supported: bits 2 or 3; d_model and d_ff multiples of 32, d_model <= 16384,
+ * d_ff <= 4096.  Prefill additionally needs bits == 2, d_model % 128 == 0 and
+ * d_ff % 64 == 0. */
+typedef struct {
+    int n_experts;
+    int d_model;
+    int d_ff;
+    int bits;
+    const uint32_t* gate_q;
+    const uint32_t* up_q;
+    const uint32_t* down_q;
+    const uint16_t* gate_s;
+    const uint16_t* up_s;
+    const uint16_t* down_s;
+} moe_experts_t;
+
+/* Bytes of workspace `op` needs for n_tokens tokens (0 if the arguments are
+ * invalid).  For MOE_OP_ROUTE, d_ff is ignored. */
+size_t moe_workspace_size(int op, int n_tokens, int d_model, int d_ff, int n_experts, int top_k);
+
+/* Router logits, top-k selection, gates and (optionally) expert buckets.
+ *
+ *   z[t][e]  = sum_d x[t][d] * w[d][e] + bias[e], accumulated in fp64
+ *   ids[t]   = the top_k experts by z in rank order; equal logits go to the
+ *              lower expert id
+ *   gates[t] = softmax over the selected logits (= softmax over all experts
+ *              renormalised over the chosen k), fp64, stored as fp32
+ *   buckets  = pairs p = t*top_k + j grouped by expert: bucket_offsets[e] is
+ *              the exclusive prefix sum of per-expert counts, with
+ *              bucket_offsets[n_experts] = n_tokens*top_k, and bucket_pairs
+ *              lists the pair ids of expert 0, expert 1, ..., each bucket in
+ *              ascending pair id.
+ *
+ *   x              device [n_tokens][d_model], fp32 or bf16 (x_dtype)
+ *   topk_ids       device int32 [n_tokens][top_k]            (output)
+ *   topk_w         device fp32  [n_tokens][top_k]            (output)
+ *   bucket_offsets device int32 [n_experts + 1] or NULL      (output)
+ *   bucket_pairs   device int32 [n_tokens * top_k] or NULL   (output)
+ * Buckets are produced only when both bucket pointers are non-NULL. */
+int moe_route(const moe_router_t* router, const void* x, int x_dtype, int n_tokens,
+              int32_t* topk_ids, float* topk_w, int32_t* bucket_offsets, int32_t* bucket_pairs,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN and combine for a small batch (decode / speculative verify).
+ *
+ *   y[t] = sum_{j < top_k} topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t])
+ *   FFN_e(v) = (silu(v Wg_e) * (v Wu_e)) Wd_e,  silu(g) = g / (1 + exp(-g))
+ * with weights dequantised exactly, fp32 accumulation, and the slot sum in
+ * ascending j.  Each distinct expert's weights are read once per call and
+ * shared by the tokens that chose it.  Results for a token do not depend on
+ * n_tokens or on the other tokens (bitwise).
+ *
+ *   x        device [n_tokens][d_model], fp32 or bf16
+ *   topk_ids device int32 [n_tokens][top_k], each id in [0, n_experts), no
+ *            id repeated within a token
+ *   topk_w   device fp32 [n_tokens][top_k]
+ *   y        device fp32 [n_tokens][d_model] (output)
+ * Supported: 1 <= n_tokens <= 8, top_k <= 64. */
+int moe_ffn_decode(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens,
+                   const int32_t* topk_ids, const float* topk_w, int top_k, float* y,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN and combine for a prefill chunk, as grouped GEMMs over the
+ * expert buckets produced by moe_route.  Same result as moe_ffn_decode
+ * (within fp16-operand rounding: activations and the SwiGLU intermediate
+ * enter the matrix cores as fp16, accumulation is fp32).
+ *
+ *   x              device [n_tokens][d_model], fp32 or bf16
+ *   topk_w         device fp32 [n_tokens][top_k], indexed by pair id
+ *   bucket_offsets device int32 [n_experts + 1]   (from moe_route)
+ *   bucket_pairs   device int32 [n_tokens*top_k]  (from moe_route)
+ *   y              device fp32 [n_tokens][d_model] (output)
+ * Supported: n_tokens >= 1, bits == 2 (see moe_experts_t). */
+int moe_ffn_prefill(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens,
+                    const float* topk_w, int top_k, const int32_t* bucket_offsets,
+                    const int32_t* bucket_pairs, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Residual update and RMSNorm between chained layers:
+ *   h[t] += y[t];  u[t] = h[t] / sqrt(mean(h[t]^2) + eps)
+ * with the mean square in fp64 and gamma = 1.  h, y, u: device fp32
+ * [n_tokens][d]; y may be NULL (norm only); u may alias nothing. */
+int moe_residual_rmsnorm(float* h, const float* y, float* u, int n_tokens, int d, double eps, void* stream);
+
+/* Static English text for a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

@@ -1,0 +1,203 @@
+"""Python binding of ``libmoe_ffn.so`` (the C ABI in ``include/moe_ffn.h``).
+
+Argument marshalling only: tensors are passed as device pointers with the
+current torch stream; every step of the computation runs in the library's
+HIP kernels.  Importing the package loads the library and raises if it has
+not been built (``python -m quantized_moe_expert_lds_amd.build``): there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
+    "MOE_F32", "MOE_BF16", "MOE_OP_ROUTE", "MOE_OP_DECODE", "MOE_OP_PREFILL",
+    "MoeError", "Router", "Experts", "lib_path", "library",
+    "moe_workspace_size", "workspace", "moe_route", "moe_ffn_decode", "moe_ffn_prefill",
+    "moe_residual_rmsnorm", "moe_status_string", "EXPORTED_SYMBOLS",
+]
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_DEVICE, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
+
+EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_ffn_decode", "moe_ffn_prefill",
+                    "moe_residual_rmsnorm", "moe_status_string")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "lib", "libmoe_ffn.so")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_status_string(status)} (status {status})")
+        self.status = status
+
+
+class _RouterT(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int), ("n_experts", ctypes.c_int), ("top_k", ctypes.c_int),
+                ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class _ExpertsT(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int), ("d_model", ctypes.c_int), ("d_ff", ctypes.c_int),
+                ("bits", ctypes.c_int),
+                ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
+                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with `python -m quantized_moe_expert_lds_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    P, I, Z, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    lib.moe_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.moe_workspace_size.restype = Z
+    lib.moe_route.argtypes = [ctypes.POINTER(_RouterT), P, I, I, P, P, P, P, P, Z, P]
+    lib.moe_route.restype = I
+    lib.moe_ffn_decode.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, P, I, P, P, Z, P]
+    lib.moe_ffn_decode.restype = I
+    lib.moe_ffn_prefill.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, I, P, P, P, P, Z, P]
+    lib.moe_ffn_prefill.restype = I
+    lib.moe_residual_rmsnorm.argtypes = [P, P, P, I, I, D, P]
+    lib.moe_residual_rmsnorm.restype = I
+    lib.moe_status_string.argtypes = [I]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+library = _load()
+
+
+def moe_status_string(status: int) -> str:
+    return library.moe_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+@dataclass
+class Router:
+    """Router of one layer: ``w`` fp32 [d_model][n_experts], ``bias`` fp32
+    [n_experts] or None."""
+    w: torch.Tensor
+    bias: Optional[torch.Tensor]
+    top_k: int
+    _c: _RouterT = field(init=False, repr=False)
+
+    def __post_init__(self):
+        d, e = self.w.shape
+        self._c = _RouterT(d, e, self.top_k, self.w.data_ptr(), 0 if self.bias is None else self.bias.data_ptr())
+
+    @property
+    def d_model(self) -> int:
+        return self.w.shape[0]
+
+    @property
+    def n_experts(self) -> int:
+        return self.w.shape[1]
+
+
+@dataclass
+class Experts:
+    """Stored experts of one layer: codes int32 [E][N][K/32][words] and fp16
+    scale bits int16 [E][N][K/32] for gate, up (N = d_ff, K = d_model) and
+    down (N = d_model, K = d_ff)."""
+    gate_q: torch.Tensor
+    up_q: torch.Tensor
+    down_q: torch.Tensor
+    gate_s: torch.Tensor
+    up_s: torch.Tensor
+    down_s: torch.Tensor
+    bits: int
+    _c: _ExpertsT = field(init=False, repr=False)
+
+    def __post_init__(self):
+        e, f, nkb = self.gate_s.shape
+        self._c = _ExpertsT(e, nkb * 32, f, self.bits,
+                            self.gate_q.data_ptr(), self.up_q.data_ptr(), self.down_q.data_ptr(),
+                            self.gate_s.data_ptr(), self.up_s.data_ptr(), self.down_s.data_ptr())
+
+    @property
+    def n_experts(self) -> int:
+        return self._c.n_experts
+
+    @property
+    def d_model(self) -> int:
+        return self._c.d_model
+
+    @property
+    def d_ff(self) -> int:
+        return self._c.d_ff
+
+
+def moe_workspace_size(op: int, n_tokens: int, d_model: int, d_ff: int, n_experts: int, top_k: int) -> int:
+    return int(library.moe_workspace_size(op, n_tokens, d_model, d_ff, n_experts, top_k))
+
+
+def workspace(op: int, n_tokens: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
+              device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of the size ``op`` needs (torch allocations are
+    256-byte aligned)."""
+    n = moe_workspace_size(op, n_tokens, d_model, d_ff, n_experts, top_k)
+    if n == 0:
+        raise MoeError("moe_workspace_size", MOE_ERR_ARG)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_route(router: Router, x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+              bucket_offsets: Optional[torch.Tensor] = None, bucket_pairs: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    st = library.moe_route(ctypes.byref(router._c), _ptr(x), _dtype(x), x.shape[0], _ptr(topk_ids), _ptr(topk_w),
+                           _ptr(bucket_offsets), _ptr(bucket_pairs), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_ffn_decode(experts: Experts, x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                   y: torch.Tensor, ws: Optional[torch.Tensor], stream=None) -> None:
+    st = library.moe_ffn_decode(ctypes.byref(experts._c), _ptr(x), _dtype(x), x.shape[0], _ptr(topk_ids),
+                                _ptr(topk_w), topk_ids.shape[1], _ptr(y), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream))
+    _check("moe_ffn_decode", st)
+
+
+def moe_ffn_prefill(experts: Experts, x: torch.Tensor, topk_w: torch.Tensor, bucket_offsets: torch.Tensor,
+                    bucket_pairs: torch.Tensor, y: torch.Tensor, ws: Optional[torch.Tensor], stream=None) -> None:
+    st = library.moe_ffn_prefill(ctypes.byref(experts._c), _ptr(x), _dtype(x), x.shape[0], _ptr(topk_w),
+                                 topk_w.shape[1], _ptr(bucket_offsets), _ptr(bucket_pairs), _ptr(y), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream))
+    _check("moe_ffn_prefill", st)
+
+
+def moe_residual_rmsnorm(h: torch.Tensor, y: Optional[torch.Tensor], u: torch.Tensor, eps: float = 1e-6,
+                         stream=None) -> None:
+    st = library.moe_residual_rmsnorm(_ptr(h), _ptr(y), _ptr(u), h.shape[0], h.shape[1], float(eps),
+                                      _stream(stream))
+    _check("moe_residual_rmsnorm", st)

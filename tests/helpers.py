@@ -1,0 +1,58 @@
+"""Shared helpers for the GPU parity tests (device model setup, oracle-side
+expert lookup, the row-normalised error metric)."""
+from __future__ import annotations
+
+import numpy as np
+
+import moe_inputs as mi
+
+TOL = 2e-3          # max over rows of max|y_gpu - y_ref| / max|y_ref|
+
+
+def row_rel_err(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    num = np.max(np.abs(got - want), axis=-1)
+    den = np.maximum(np.max(np.abs(want), axis=-1), 1e-30)
+    return float(np.max(num / den))
+
+
+_EXPERT_CACHE: dict = {}
+
+
+def host_expert(wl_name: str, layer: int, expert: int, bits: int):
+    """Stored (gate, up, down) of one expert from the host generator."""
+    key = (wl_name, layer, expert, bits)
+    if key not in _EXPERT_CACHE:
+        wl = mi.WORKLOADS[wl_name]
+        _EXPERT_CACHE[key] = tuple(mi.expert_tensor_host(wl, layer, t, expert, bits)
+                                   for t in (mi.GATE, mi.UP, mi.DOWN))
+    return _EXPERT_CACHE[key]
+
+
+def host_expert_cache_put(key, value) -> None:
+    _EXPERT_CACHE[tuple(key)] = value
+
+
+def host_expert_cache_clear() -> None:
+    _EXPERT_CACHE.clear()
+
+
+def oracle_experts(wl: mi.Workload, layer: int, bits: int | None = None):
+    bits = wl.bits if bits is None else bits
+    return lambda e: host_expert(wl.name, layer, int(e), bits)
+
+
+def device_layers(wl, n_layers=None, bits=None, device="cuda"):
+    """[(Router, Experts)] for the first n_layers layers of a workload."""
+    import quantized_moe_expert_lds_amd as q
+    import moe_inputs.gpu as g
+    bits = wl.bits if bits is None else bits
+    ex = g.expert_tensors(wl, n_layers, bits, device)
+    rt = g.routers(wl, n_layers, device)
+    layers = []
+    for l, (w, b) in enumerate(rt):
+        layers.append((q.Router(w, b if wl.zipf_bias else None, wl.top_k),
+                       q.Experts(ex["gate_q"][l], ex["up_q"][l], ex["down_q"][l],
+                                 ex["gate_s"][l], ex["up_s"][l], ex["down_s"][l], bits)))
+    return layers, ex, rt
