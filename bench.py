@@ -4,7 +4,8 @@ Headline workload: one 48-layer decode step at batch 1 (512 experts per
 layer, d_model 2048, d_ff 768, top-10, 2-bit block-quantised experts, fp32
 residual stream with RMSNorm between layers).  A step is, for every layer:
 router logits + top-k + gates, the expert FFN with the weighted combine, and
-the residual update + RMSNorm -- all on the GPU, captured in one HIP graph.
+the residual update + RMSNorm -- all on the GPU in one persistent kernel
+launch (moe_decode_stack).
 Inputs (all 24,576 experts, ~36 GB) are resident in HBM before timing; each
 step consumes a different synthetic token.
 
@@ -38,104 +39,60 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_layers(q, wl, bits=None):
+def build_stack(q, torch, wl, bits=None):
+    """Every layer of a workload as one Stack, generated in HBM."""
     import moe_inputs.gpu as g
     bits = wl.bits if bits is None else bits
     ex = g.expert_tensors(wl, None, bits)
     rt = g.routers(wl)
-    layers = []
-    for l, (w, b) in enumerate(rt):
-        layers.append((q.Router(w, b if wl.zipf_bias else None, wl.top_k),
-                       q.Experts(ex["gate_q"][l], ex["up_q"][l], ex["down_q"][l],
-                                 ex["gate_s"][l], ex["up_s"][l], ex["down_s"][l], bits)))
-    return layers, ex, rt
+    rw = torch.stack([w for w, _ in rt]).contiguous()
+    rb = torch.stack([b for _, b in rt]).contiguous() if wl.zipf_bias else None
+    del rt
+    st = q.Stack(rw, rb, ex["gate_q"], ex["up_q"], ex["down_q"], ex["gate_s"], ex["up_s"], ex["down_s"],
+                 bits, wl.top_k)
+    return st, (ex, rw, rb)
 
 
-class DecodeStep:
-    """48-layer decode/verify step: route -> expert FFN -> residual + RMSNorm
-    per layer, on one stream."""
-
-    def __init__(self, q, torch, layers, T):
-        self.q, self.torch, self.layers, self.T = q, torch, layers, T
-        r0, e0 = layers[0]
-        D, F, E, K = e0.d_model, e0.d_ff, e0.n_experts, r0.top_k
-        dev = "cuda"
-        self.xin = torch.zeros((T, D), device=dev)
-        self.h = torch.empty((T, D), device=dev)
-        self.u = torch.empty((T, D), device=dev)
-        self.y = torch.empty((T, D), device=dev)
-        self.ids = torch.empty((T, K), dtype=torch.int32, device=dev)
-        self.w = torch.empty((T, K), device=dev)
-        self.ws_r = q.workspace(q.MOE_OP_ROUTE, T, D, F, E, K)
-        self.ws_d = q.workspace(q.MOE_OP_DECODE, T, D, F, E, K)
-        self.ids_per_layer = [torch.empty((T, K), dtype=torch.int32, device=dev) for _ in layers]
-        self.w_per_layer = [torch.empty((T, K), device=dev) for _ in layers]
-
-    def run(self, keep_routing=False):
-        q = self.q
-        self.h.copy_(self.xin)
-        for l, (router, experts) in enumerate(self.layers):
-            inp = self.h if l == 0 else self.u
-            ids = self.ids_per_layer[l] if keep_routing else self.ids
-            w = self.w_per_layer[l] if keep_routing else self.w
-            q.moe_route(router, inp, ids, w, None, None, self.ws_r)
-            q.moe_ffn_decode(experts, inp, ids, w, self.y, self.ws_d)
-            q.moe_residual_rmsnorm(self.h, self.y, self.u, 1e-6)
-
-    def capture(self):
-        torch = self.torch
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            self.run()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.run()
-        torch.cuda.synchronize()
-        return g
-
-
-def time_graph_steps(torch, g, step, xs, warmup, steps):
-    """Time `steps` replays (each fed a new token) after `warmup` replays."""
-    for i in range(warmup):
-        step.xin.copy_(xs[i % len(xs)])
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step.xin.copy_(xs[(warmup + i) % len(xs)])
-        g.replay()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
-
-
-def decode_ffn_roofline(q, torch, step, layers, reps=3):
-    """Average duration of the expert-FFN call (moe_ffn_decode) over all
-    layers of a recorded step, timed with events on its own stream; each
-    call touches a different layer's experts, so successive calls do not hit
-    in the 256 MB MALL.  Returns (avg seconds, algorithmic bytes per call)."""
+def bench_stack(q, torch, wl, steps, warmup, bits=None):
+    """Time `steps` decode steps (one moe_decode_stack launch each, a new
+    token batch per step) after `warmup` steps.  Returns wall seconds per step,
+    the average kernel duration from HIP events on the launch stream, and the
+    algorithmic HBM bytes per launch (packed codes + scales of the distinct
+    experts each layer selects, the router matrices, activations)."""
+    import moe_inputs.gpu as g
+    st, keep = build_stack(q, torch, wl, bits)
+    T, L, K, D, E = wl.n_tokens, st.n_layers, wl.top_k, wl.d_model, wl.n_experts
+    n_tok = steps + warmup
+    xs = torch.stack([g.activations(wl, stream=s) for s in range(n_tok)])
+    h = torch.empty((T, D), device="cuda")
+    ws = q.stack_workspace(st, T)
+    ids = torch.empty((steps, L, T, K), dtype=torch.int32, device="cuda")
+    gw = torch.empty((steps, L, T, K), device="cuda")
     stream = torch.cuda.current_stream()
-    durs = []
-    nbytes = []
-    T = step.T
-    for _ in range(reps):
-        evs = []
-        for l, (router, experts) in enumerate(layers):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            q.moe_ffn_decode(experts, step.u, step.ids_per_layer[l], step.w_per_layer[l], step.y, step.ws_d)
-            b.record(stream)
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        durs += [a.elapsed_time(b) * 1e-3 for a, b in evs]
-    for l, (router, experts) in enumerate(layers):
-        uniq = torch.unique(step.ids_per_layer[l]).numel()
-        per_expert = (3 * experts.d_model * experts.d_ff) // 32 * (4 * (2 if experts._c.bits == 2 else 3) + 2)
-        nbytes.append(uniq * per_expert + T * experts.d_model * (4 + 4) + T * router.top_k * 8)
-    return float(np.mean(durs)), float(np.mean(nbytes))
+    for i in range(warmup):
+        q.moe_decode_stack(st, xs[i], h, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        q.moe_decode_stack(st, xs[warmup + i], h, ws, ids[i], gw[i])
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    err = int(ws[q.MOE_STACK_ERROR_OFFSET:q.MOE_STACK_ERROR_OFFSET + 4].view(torch.int32).item())
+    if err:
+        raise RuntimeError("moe_decode_stack reported a barrier timeout")
+    ids_np = ids.cpu().numpy()
+    uniq = np.array([[len(np.unique(ids_np[i, l])) for l in range(L)] for i in range(steps)])
+    bits_ = st._c.bits
+    per_expert = 3 * D * wl.d_ff // 32 * (4 * (2 if bits_ == 2 else 3) + 2)
+    nbytes = float(uniq.sum(axis=1).mean()) * per_expert + L * E * D * 4 + (E * 4 * L if wl.zipf_bias else 0) \
+        + 2 * T * D * 4
+    del st, keep, xs, ws
+    torch.cuda.empty_cache()
+    return wall, kern, nbytes, float(uniq.mean())
 
 
 def cpu_baseline(n_layers_sample=12):
@@ -225,17 +182,11 @@ def bench_prefill(q, torch, steps=5, warmup=2):
 
 def bench_verify(q, torch, steps=10, warmup=3):
     import moe_inputs as mi
-    import moe_inputs.gpu as g
     wl = mi.WORKLOADS["verify4_3bit"]
-    layers, ex, rt = build_layers(q, wl)
-    step = DecodeStep(q, torch, layers, wl.n_tokens)
-    xs = [g.activations(wl, stream=s) for s in range(8)]
-    gr = step.capture()
-    dt = time_graph_steps(torch, gr, step, xs, warmup, steps)
-    res = {"workload": "verify4_3bit", "tokens_per_s": wl.n_tokens / dt, "ms_per_step": dt * 1e3}
-    del layers, ex, rt, gr, step
-    torch.cuda.empty_cache()
-    return res
+    wall, kern, nbytes, uniq = bench_stack(q, torch, wl, steps, warmup)
+    return {"workload": "verify4_3bit", "tokens_per_s": wl.n_tokens / wall, "ms_per_step": wall * 1e3,
+            "kernel_ms": kern * 1e3, "distinct_experts_per_layer": uniq,
+            "hbm_gbs": nbytes / kern / 1e9, "hbm_frac": nbytes / kern / 1e9 / HBM_PEAK_GBS}
 
 
 def main():
@@ -258,32 +209,16 @@ def main():
 
     torch.cuda.set_device(0)
     wl = mi.WORKLOADS["decode_48layer"]
-    log("generating 48 x 512 experts in HBM")
-    layers, ex, rt = build_layers(q, wl)
-    step = DecodeStep(q, torch, layers, 1)
-    n_tok = max(64, args.steps + args.warmup)
-    xs = [g.activations(wl, stream=s) for s in range(n_tok)]
-    log("capturing the 48-layer step")
-    gr = step.capture()
-    dt = time_graph_steps(torch, gr, step, xs, args.warmup, args.steps)
-    log(f"decode step {dt * 1e6:.1f} us")
-
-    # routing of one eager step kept per layer, for the FFN roofline timing
-    step.xin.copy_(xs[0])
-    step.run(keep_routing=True)
-    torch.cuda.synchronize()
-    ffn_s, ffn_bytes = decode_ffn_roofline(q, torch, step, layers)
-    achieved = ffn_bytes / ffn_s / 1e9
-    log(f"expert FFN call {ffn_s * 1e6:.2f} us, {achieved:.0f} GB/s")
+    log("48-layer decode, batch 1: generating 48 x 512 experts in HBM and timing")
+    dt, kern, nbytes, uniq = bench_stack(q, torch, wl, args.steps, args.warmup)
+    achieved = nbytes / kern / 1e9
+    log(f"decode step {dt * 1e6:.1f} us wall, kernel {kern * 1e6:.1f} us, {achieved:.0f} GB/s")
 
     also = {}
     if not args.no_also:
-        del gr
         log("prefill 8192")
         also["prefill"] = bench_prefill(q, torch)
         log("verify 4 tokens 3-bit")
-        del layers, ex, rt, step
-        torch.cuda.empty_cache()
         also["verify"] = bench_verify(q, torch)
 
     cpu = None
@@ -307,9 +242,11 @@ def main():
                 "Zipf-biased router)",
         "config": {"workload": "decode_48layer", "layers": 48, "experts_per_layer": 512, "d_model": 2048,
                    "d_ff": 768, "top_k": 10, "batch": 1, "weight_bits": 2, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "moe_ffn_decode (gate/up + down kernels)",
+        "roofline": {"bound": "hbm", "kernel": "decode_stack_kernel (all 48 layers, one launch)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": nbytes, "kernel_us": kern * 1e6,
+                     "distinct_experts_per_layer": uniq},
         "cpu_baseline": cpu,
         "also": also,
     }

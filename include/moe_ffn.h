@@ -28,9 +28,9 @@
  *   (except MOE_ERR_HIP, reported when a launch itself fails).  Nothing throws.
  * - Workspaces: `ws` is device scratch of at least moe_workspace_size(...)
  *   bytes, 256-byte aligned.  It must be zero-filled once before its first
- *   use; every call leaves the counters it uses at zero again, so one zeroed
- *   workspace serves any number of calls.  Calls that run concurrently need
- *   distinct workspaces.
+ *   use; every call leaves the synchronisation counters it uses at zero
+ *   again, so one zeroed workspace serves any number of calls.  Calls that
+ *   run concurrently need distinct workspaces.
  * - Inputs are assumed finite; NaN logits give unspecified routing.
  *
  * Stored expert weights
@@ -72,8 +72,14 @@ extern "C" {
 #define MOE_OP_DECODE  1
 #define MOE_OP_PREFILL 2
 
+/* byte offset in a moe_decode_stack workspace of the int that becomes
+ * nonzero if a grid barrier timed out (see moe_decode_stack) */
+#define MOE_STACK_ERROR_OFFSET 2304
+
 /* Linear router of one layer.
- *   w    device fp32 [d_model][n_experts] row-major
+ *   w    device fp32 [n_experts][d_model]: expert-major, row e is the router
+ *        vector of expert e (the transpose of the [d_model x n_experts]
+ *        matrix in z = x W)
  *   bias device fp32 [n_experts], or NULL for no bias
  * Supported: d_model multiple of 32 and <= 16384, 1 <= top_k <= min(n_experts, 64),
  * n_experts <= 1024. */
@@ -102,13 +108,35 @@ typedef struct {
     const uint16_t* down_s;
 } moe_experts_t;
 
+/* A stack of MoE layers whose tensors are stored back to back, layer-major
+ * (layer l of each tensor starts at l times that tensor's per-layer size).
+ *   router_w device fp32 [L][n_experts][d_model] (expert-major rows)
+ *   router_b device fp32 [L][n_experts], or NULL
+ *   *_q, *_s device, [L] x the per-layer layouts of moe_experts_t */
+typedef struct {
+    int n_layers;
+    int n_experts;
+    int d_model;
+    int d_ff;
+    int top_k;
+    int bits;
+    const float* router_w;
+    const float* router_b;
+    const uint32_t* gate_q;
+    const uint32_t* up_q;
+    const uint32_t* down_q;
+    const uint16_t* gate_s;
+    const uint16_t* up_s;
+    const uint16_t* down_s;
+} moe_stack_t;
+
 /* Bytes of workspace `op` needs for n_tokens tokens (0 if the arguments are
  * invalid).  For MOE_OP_ROUTE, d_ff is ignored. */
 size_t moe_workspace_size(int op, int n_tokens, int d_model, int d_ff, int n_experts, int top_k);
 
 /* Router logits, top-k selection, gates and (optionally) expert buckets.
  *
- *   z[t][e]  = sum_d x[t][d] * w[d][e] + bias[e], accumulated in fp64
+ *   z[t][e]  = sum_d x[t][d] * w[e][d] + bias[e], accumulated in fp64
  *   ids[t]   = the top_k experts by z in rank order; equal logits go to the
  *              lower expert id
  *   gates[t] = softmax over the selected logits (= softmax over all experts
@@ -168,6 +196,39 @@ int moe_ffn_prefill(const moe_experts_t* experts, const void* x, int x_dtype, in
  * with the mean square in fp64 and gamma = 1.  h, y, u: device fp32
  * [n_tokens][d]; y may be NULL (norm only); u may alias nothing. */
 int moe_residual_rmsnorm(float* h, const float* y, float* u, int n_tokens, int d, double eps, void* stream);
+
+/* Bytes of workspace moe_decode_stack needs for `model` and n_tokens tokens
+ * (sized for up to 1024 compute units; 0 if the arguments are invalid). */
+size_t moe_stack_workspace_size(const moe_stack_t* model, int n_tokens);
+
+/* One decode (or speculative-verify) step through every layer of a stack:
+ *   h_0 = x;  for l = 0 .. L-1:
+ *     u_l = h_l if l == 0, else h_l / sqrt(mean(h_l^2) + eps)   (fp64 mean)
+ *     ids_l, gates_l = moe_route(layer l, u_l)
+ *     h_{l+1} = h_l + moe_ffn_decode(layer l, u_l, ids_l, gates_l)   (fp32)
+ *   h_out = h_L
+ * Routing follows moe_route (fp64 logits, ties to the lower id; the logits
+ * are summed in a different order than in moe_route, so a logit can differ
+ * in its last bits) and the expert math follows moe_ffn_decode.  Results
+ * for a token do not depend on n_tokens (bitwise).
+ *
+ * Runs as one cooperative launch with one workgroup per compute unit that
+ * stays resident for all layers; layers are separated by grid barriers
+ * instead of kernel boundaries.  If the workgroups cannot all be resident
+ * the launch fails with MOE_ERR_HIP; should a barrier nevertheless wait
+ * longer than a few seconds, the kernel stops, the int at byte offset
+ * MOE_STACK_ERROR_OFFSET of ws becomes nonzero, the outputs are undefined and
+ * ws must be zero-filled again before reuse.
+ *
+ *   x            device [n_tokens][d_model], fp32 or bf16
+ *   h_out        device fp32 [n_tokens][d_model] (output)
+ *   topk_ids_out device int32 [L][n_tokens][top_k] or NULL (output)
+ *   topk_w_out   device fp32  [L][n_tokens][top_k] or NULL (output; both or neither)
+ * Supported: 1 <= n_tokens <= 8, d_model and d_ff multiples of 32 and
+ * <= 4096, n_experts <= min(1024, 4 x compute units), top_k <= min(n_experts, 64). */
+int moe_decode_stack(const moe_stack_t* model, const void* x, int x_dtype, int n_tokens, double eps,
+                     float* h_out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Static English text for a status code. */
 const char* moe_status_string(int status);

@@ -21,7 +21,7 @@ def _library():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
-            raise ImportError(f"{_LIB} is missing: build it with `python -m quantized_moe_expert_lds_amd.build`")
+            raise ImportError(f"{_LIB} is missing: build it with `python quantized_moe_expert_lds_amd/build.py`")
         _lib = ctypes.CDLL(_LIB)
         P, I = ctypes.c_void_p, ctypes.c_int
         _lib.moegen_expert_tensors.argtypes = [P, I, I, I, I, ctypes.c_float, P, P, P, P]
@@ -68,12 +68,14 @@ def expert_tensors(wl: mi.Workload, n_layers: int | None = None, bits: int | Non
 
 
 def routers(wl: mi.Workload, n_layers: int | None = None, device="cuda"):
-    """[(w fp32 [D][E], bias fp32 [E])] per layer on the device."""
+    """[(w, bias fp32 [E])] per layer on the device, with the router matrix
+    stored expert-major: w fp32 [E][D] is the transpose of the host
+    generator's [D][E] matrix (same values)."""
     L = wl.n_layers if n_layers is None else n_layers
     out = []
     for layer in range(L):
         w, b = mi.router_host(wl, layer)
-        out.append((torch.from_numpy(w).to(device), torch.from_numpy(b).to(device)))
+        out.append((torch.from_numpy(np.ascontiguousarray(w.T)).to(device), torch.from_numpy(b).to(device)))
     return out
 
 

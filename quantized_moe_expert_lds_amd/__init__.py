@@ -3,7 +3,7 @@
 Argument marshalling only: tensors are passed as device pointers with the
 current torch stream; every step of the computation runs in the library's
 HIP kernels.  Importing the package loads the library and raises if it has
-not been built (``python -m quantized_moe_expert_lds_amd.build``): there is
+not been built (``python quantized_moe_expert_lds_amd/build.py``): there is
 no fallback path.
 """
 from __future__ import annotations
@@ -17,18 +17,20 @@ import torch
 
 __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
-    "MOE_F32", "MOE_BF16", "MOE_OP_ROUTE", "MOE_OP_DECODE", "MOE_OP_PREFILL",
-    "MoeError", "Router", "Experts", "lib_path", "library",
-    "moe_workspace_size", "workspace", "moe_route", "moe_ffn_decode", "moe_ffn_prefill",
+    "MOE_F32", "MOE_BF16", "MOE_OP_ROUTE", "MOE_OP_DECODE", "MOE_OP_PREFILL", "moe_stack_workspace_size",
+    "stack_workspace",
+    "MOE_STACK_ERROR_OFFSET", "MoeError", "Router", "Experts", "Stack", "lib_path", "library",
+    "moe_workspace_size", "workspace", "moe_route", "moe_ffn_decode", "moe_ffn_prefill", "moe_decode_stack",
     "moe_residual_rmsnorm", "moe_status_string", "EXPORTED_SYMBOLS",
 ]
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_DEVICE, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
+MOE_STACK_ERROR_OFFSET = 2304
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_ffn_decode", "moe_ffn_prefill",
-                    "moe_residual_rmsnorm", "moe_status_string")
+                    "moe_stack_workspace_size", "moe_decode_stack", "moe_residual_rmsnorm", "moe_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "lib", "libmoe_ffn.so")
@@ -52,9 +54,17 @@ class _ExpertsT(ctypes.Structure):
                 ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
 
 
+class _StackT(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("n_experts", ctypes.c_int), ("d_model", ctypes.c_int),
+                ("d_ff", ctypes.c_int), ("top_k", ctypes.c_int), ("bits", ctypes.c_int),
+                ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
+                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(lib_path):
-        raise ImportError(f"{lib_path} is missing: build it with `python -m quantized_moe_expert_lds_amd.build`")
+        raise ImportError(f"{lib_path} is missing: build it with `python quantized_moe_expert_lds_amd/build.py`")
     lib = ctypes.CDLL(lib_path)
     P, I, Z, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
     lib.moe_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -65,6 +75,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_ffn_decode.restype = I
     lib.moe_ffn_prefill.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, I, P, P, P, P, Z, P]
     lib.moe_ffn_prefill.restype = I
+    lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_StackT), I]
+    lib.moe_stack_workspace_size.restype = Z
+    lib.moe_decode_stack.argtypes = [ctypes.POINTER(_StackT), P, I, I, D, P, P, P, P, Z, P]
+    lib.moe_decode_stack.restype = I
     lib.moe_residual_rmsnorm.argtypes = [P, P, P, I, I, D, P]
     lib.moe_residual_rmsnorm.restype = I
     lib.moe_status_string.argtypes = [I]
@@ -104,24 +118,24 @@ def _check(fn: str, status: int) -> None:
 
 @dataclass
 class Router:
-    """Router of one layer: ``w`` fp32 [d_model][n_experts], ``bias`` fp32
-    [n_experts] or None."""
+    """Router of one layer: ``w`` fp32 [n_experts][d_model] (expert-major: row
+    e is expert e's router vector), ``bias`` fp32 [n_experts] or None."""
     w: torch.Tensor
     bias: Optional[torch.Tensor]
     top_k: int
     _c: _RouterT = field(init=False, repr=False)
 
     def __post_init__(self):
-        d, e = self.w.shape
+        e, d = self.w.shape
         self._c = _RouterT(d, e, self.top_k, self.w.data_ptr(), 0 if self.bias is None else self.bias.data_ptr())
 
     @property
     def d_model(self) -> int:
-        return self.w.shape[0]
+        return self.w.shape[1]
 
     @property
     def n_experts(self) -> int:
-        return self.w.shape[1]
+        return self.w.shape[0]
 
 
 @dataclass
@@ -143,6 +157,49 @@ class Experts:
         self._c = _ExpertsT(e, nkb * 32, f, self.bits,
                             self.gate_q.data_ptr(), self.up_q.data_ptr(), self.down_q.data_ptr(),
                             self.gate_s.data_ptr(), self.up_s.data_ptr(), self.down_s.data_ptr())
+
+    @property
+    def n_experts(self) -> int:
+        return self._c.n_experts
+
+    @property
+    def d_model(self) -> int:
+        return self._c.d_model
+
+    @property
+    def d_ff(self) -> int:
+        return self._c.d_ff
+
+
+@dataclass
+class Stack:
+    """All layers of a model, each tensor stored layer-major: router_w fp32
+    [L][E][D] (expert-major rows), router_b fp32 [L][E] or None, codes int32
+    [L][E][N][K/32][words] and scale bits int16 [L][E][N][K/32] for gate, up
+    and down."""
+    router_w: torch.Tensor
+    router_b: Optional[torch.Tensor]
+    gate_q: torch.Tensor
+    up_q: torch.Tensor
+    down_q: torch.Tensor
+    gate_s: torch.Tensor
+    up_s: torch.Tensor
+    down_s: torch.Tensor
+    bits: int
+    top_k: int
+    _c: _StackT = field(init=False, repr=False)
+
+    def __post_init__(self):
+        L, E, D = self.router_w.shape
+        F = self.gate_s.shape[2]
+        self._c = _StackT(L, E, D, F, self.top_k, self.bits, self.router_w.data_ptr(),
+                          0 if self.router_b is None else self.router_b.data_ptr(),
+                          self.gate_q.data_ptr(), self.up_q.data_ptr(), self.down_q.data_ptr(),
+                          self.gate_s.data_ptr(), self.up_s.data_ptr(), self.down_s.data_ptr())
+
+    @property
+    def n_layers(self) -> int:
+        return self._c.n_layers
 
     @property
     def n_experts(self) -> int:
@@ -194,6 +251,27 @@ def moe_ffn_prefill(experts: Experts, x: torch.Tensor, topk_w: torch.Tensor, buc
                                  topk_w.shape[1], _ptr(bucket_offsets), _ptr(bucket_pairs), _ptr(y), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(stream))
     _check("moe_ffn_prefill", st)
+
+
+def moe_stack_workspace_size(stack: Stack, n_tokens: int) -> int:
+    return int(library.moe_stack_workspace_size(ctypes.byref(stack._c), n_tokens))
+
+
+def stack_workspace(stack: Stack, n_tokens: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for moe_decode_stack."""
+    n = moe_stack_workspace_size(stack, n_tokens)
+    if n == 0:
+        raise MoeError("moe_stack_workspace_size", MOE_ERR_ARG)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_decode_stack(stack: Stack, x: torch.Tensor, h_out: torch.Tensor, ws: Optional[torch.Tensor],
+                     topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                     eps: float = 1e-6, stream=None) -> None:
+    st = library.moe_decode_stack(ctypes.byref(stack._c), _ptr(x), _dtype(x), x.shape[0], float(eps), _ptr(h_out),
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream))
+    _check("moe_decode_stack", st)
 
 
 def moe_residual_rmsnorm(h: torch.Tensor, y: Optional[torch.Tensor], u: torch.Tensor, eps: float = 1e-6,

@@ -1,6 +1,6 @@
 """Build the HIP shared libraries in-tree for gfx950.
 
-    python -m quantized_moe_expert_lds_amd.build
+    python quantized_moe_expert_lds_amd/build.py
 
 produces ``quantized_moe_expert_lds_amd/lib/libmoe_ffn.so`` (the MoE FFN
 library behind ``include/moe_ffn.h``) and ``moe_inputs/lib/libmoe_inputs.so``

@@ -63,6 +63,24 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 size_t decode_ws_bytes(int T, int F, int K) { return decode_ws_layout(T, F, K).total; }
 
+std::atomic<int> g_cus[kMaxDevices];       // compute units per device, 0 = unknown
+
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int coop = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,6 +96,7 @@ size_t moe_workspace_size(int op, int n_tokens, int d_model, int d_ff, int n_exp
         case MOE_OP_PREFILL:
             if (d_ff <= 0) return 0;
             return prefill_ws_layout(n_tokens, d_model, d_ff, n_experts, top_k).total;
+
         default:
             return 0;
     }
@@ -144,6 +163,42 @@ int moe_ffn_prefill(const moe_experts_t* experts, const void* x, int x_dtype, in
     if ((st = check_device())) return st;
     return hip_status(launch_prefill(*experts, x, xf, n_tokens, topk_w, top_k, bucket_offsets, bucket_pairs, y,
                                      (char*)ws, L, (hipStream_t)stream));
+}
+
+size_t moe_stack_workspace_size(const moe_stack_t* m, int n_tokens) {
+    if (!m || n_tokens <= 0 || m->n_layers <= 0 || m->n_experts <= 0 || m->d_model <= 0 || m->d_ff <= 0 ||
+        m->top_k <= 0)
+        return 0;
+    return stack_ws_layout(n_tokens, m->d_model, m->d_ff, m->n_experts, m->top_k, kStackMaxGrid, m->n_layers).total;
+}
+
+int moe_decode_stack(const moe_stack_t* m, const void* x, int x_dtype, int n_tokens, double eps, float* h_out,
+                     int32_t* ids_out, float* gates_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!m || !x || !h_out || n_tokens <= 0 || !(eps >= 0.0)) return MOE_ERR_ARG;
+    if (!m->router_w || !m->gate_q || !m->up_q || !m->down_q || !m->gate_s || !m->up_s || !m->down_s)
+        return MOE_ERR_ARG;
+    if ((ids_out == nullptr) != (gates_out == nullptr)) return MOE_ERR_ARG;
+    const int xf = dtype_flag(x_dtype);
+    if (xf < 0) return MOE_ERR_ARG;
+    const int L = m->n_layers, E = m->n_experts, D = m->d_model, F = m->d_ff, K = m->top_k;
+    if (L <= 0 || E <= 0 || D <= 0 || F <= 0 || K <= 0) return MOE_ERR_ARG;
+    if (m->bits != 2 && m->bits != 3) return MOE_ERR_UNSUPPORTED;
+    if (n_tokens > kMaxDecodeTokens || D % 32 || F % 32 || D > kStackMaxD || F > kMaxDff || E > kMaxExperts ||
+        K > E || K > kMaxTopK)
+        return MOE_ERR_UNSUPPORTED;
+    if (!ws) return MOE_ERR_WORKSPACE;
+    int st = check_device();
+    if (st) return st;
+    const int G = device_cus();
+    if (G <= 0 || G > kStackMaxGrid) return MOE_ERR_NO_DEVICE;
+    const StackWs Lw = stack_ws_layout(n_tokens, D, F, E, K, G, L);
+    if ((st = check_ws(ws, ws_bytes, Lw.total))) return st;
+    // router experts and d_model rows per workgroup
+    if ((E + G - 1) / G > 4 || (D + G - 1) / G > 32) return MOE_ERR_UNSUPPORTED;
+    if (stack_lds_bytes(n_tokens, D, F, E, K, G, m->bits, nullptr, nullptr, nullptr, nullptr, nullptr) > kStackLdsLimit)
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_decode_stack(*m, x, xf, n_tokens, h_out, ids_out, gates_out, eps, (char*)ws, Lw, G,
+                                          (hipStream_t)stream));
 }
 
 int moe_residual_rmsnorm(float* h, const float* y, float* u, int n_tokens, int d, double eps, void* stream) {

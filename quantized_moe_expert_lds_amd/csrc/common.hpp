@@ -16,9 +16,6 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxDModel = 16384;
 constexpr int kMaxDff = 4096;
 
-// router, small-batch path: 64 experts x 64 d-rows per workgroup
-constexpr int kRouteSmallE = 64;
-constexpr int kRouteSmallD = 64;
 // router, large-batch path: 64 tokens x 64 experts per workgroup, 32-row k-steps
 constexpr int kRouteTileT = 64;
 constexpr int kRouteTileE = 64;
@@ -36,7 +33,7 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ workspace map
 struct RouteWs {
-    size_t zpart, zfull, counters, hist, rank, total;
+    size_t zfull, hist, rank, total;
 };
 struct DecodeWs {
     size_t h, total;
@@ -44,18 +41,22 @@ struct DecodeWs {
 struct PrefillWs {
     size_t x16, hbuf, obuf, tiles, ntiles, total;
 };
+struct StackWs {
+    size_t sync, zbuf, hres, ssp, hbuf, total;
+};
+constexpr int kStackMaxGrid = 1024;      // workspace sized for up to this many workgroups
+constexpr int kStackMaxD = 4096;
+constexpr size_t kStackLdsLimit = 160 * 1024;
+StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L);
+size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits, int* us_off, int* part_off,
+                       int* misc_off, int* pre_off, int* wr_off);
 
 inline RouteWs route_ws_layout(int T, int D, int E, int K) {
     RouteWs w{};
     size_t off = 0;
-    const int ndc = cdiv(D, kRouteSmallD);
-    const int nec = cdiv(E, kRouteSmallE);
-    w.zpart = off;
-    off += align256(T <= kMaxDecodeTokens ? sizeof(double) * (size_t)ndc * T * E : 0);
+    (void)D;
     w.zfull = off;
     off += align256(sizeof(double) * (size_t)T * E);
-    w.counters = off;
-    off += align256(sizeof(int) * (size_t)(nec + 1));
     const size_t P = (size_t)T * K;
     const size_t nb = (P + kBucketBlock - 1) / kBucketBlock;
     w.hist = off;
@@ -110,6 +111,9 @@ hipError_t launch_decode(const moe_experts_t& ex, const void* x, int x_bf16, int
 hipError_t launch_prefill(const moe_experts_t& ex, const void* x, int x_bf16, int T, const float* gates,
                           int K, const int32_t* offsets, const int32_t* pairs, float* y, char* ws,
                           const PrefillWs& L, hipStream_t s);
+hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, int T, float* h_out,
+                               int32_t* ids_out, float* gates_out, double eps, char* ws, const StackWs& L, int G,
+                               hipStream_t s);
 hipError_t launch_residual_rmsnorm(float* h, const float* y, float* u, int T, int d, double eps,
                                    hipStream_t s);
 
@@ -160,6 +164,61 @@ __device__ __forceinline__ uint32_t codes3_pair(uint32_t w0, uint32_t w1, uint32
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ bool better(double a, int ia, double b, int ib) {
+    return a > b || (a == b && ia < ib);
+}
+
+// One wavefront selects the top-k of z[0..E) (E <= 1024) and writes ids and
+// gates.  Ranks by (z descending, id ascending); -0.0 == +0.0 by IEEE compare.
+__device__ inline void wave_topk(const double* z, int E, int K, int32_t* ids, float* gates) {
+    const int lane = threadIdx.x & 63;
+    constexpr int kPer = qmoe::kMaxExperts / 64;
+    double v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? z[e] + 0.0 : -INFINITY;
+    }
+    uint32_t taken = 0;
+    double my_sel = 0.0;
+    for (int j = 0; j < K; ++j) {
+        double bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == j) {
+            my_sel = bv;
+            ids[j] = bi;
+        }
+    }
+    // gates: softmax over the selected logits, fp64
+    const double m = __shfl(my_sel, 0, 64);
+    double p = lane < K ? exp(my_sel - m) : 0.0;
+    double sum = p;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    // every lane holds the same sum only if the butterfly is order-symmetric;
+    // take lane 0's value so all gates divide by one number
+    sum = __shfl(sum, 0, 64);
+    if (lane < K) gates[lane] = (float)(p / sum);
 }
 
 }  // namespace qmoe_dev

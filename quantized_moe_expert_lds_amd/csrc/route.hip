@@ -7,11 +7,12 @@
 // library's own design for gfx950.
 //
 // Two paths:
-//  * small batches (T <= 8, decode and verify): the 4 MB router matrix is the
-//    whole cost, so it is split over 64x64 (expert x d) tiles, one per
-//    workgroup, each reading 16 KB with 128-bit loads.  Partial sums are
-//    reduced by the last workgroup of each expert column ("last block done"
-//    counters), and the last column finisher selects the top-k.
+//  * small batches (T <= 8, decode and verify): reading the router matrix is
+//    the whole cost.  The router is stored expert-major ([E][d_model]), so
+//    each workgroup reads the contiguous rows of two experts (16 KB) with
+//    128-bit loads and produces complete logits; a second small kernel (one
+//    wavefront per token) selects the top-k.  No cross-workgroup
+//    synchronisation inside a kernel.
 //  * large batches (prefill): a tiled fp64 GEMM in which every logit is
 //    accumulated by one thread over d in ascending order with fused
 //    multiply-adds (each fp32 x fp32 product is exact in fp64, so this is the
@@ -31,171 +32,58 @@ __device__ __forceinline__ double load_x(const void* x, int x_bf16, size_t i) {
     return (double)((const float*)x)[i];
 }
 
-__device__ __forceinline__ bool better(double a, int ia, double b, int ib) {
-    return a > b || (a == b && ia < ib);
-}
-
-// One wavefront selects the top-k of z[0..E) (E <= 1024) and writes ids and
-// gates.  Ranks by (z descending, id ascending); -0.0 == +0.0 by IEEE compare.
-__device__ void wave_topk(const double* z, int E, int K, int32_t* ids, float* gates) {
-    const int lane = threadIdx.x & 63;
-    constexpr int kPer = kMaxExperts / 64;
-    double v[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? z[e] + 0.0 : -INFINITY;
-    }
-    uint32_t taken = 0;
-    double my_sel = 0.0;
-    for (int j = 0; j < K; ++j) {
-        double bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
-                bv = v[i];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const double ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == j) {
-            my_sel = bv;
-            ids[j] = bi;
-        }
-    }
-    // gates: softmax over the selected logits, fp64
-    const double m = __shfl(my_sel, 0, 64);
-    double p = lane < K ? exp(my_sel - m) : 0.0;
-    double sum = p;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    // every lane holds the same sum only if the butterfly is order-symmetric;
-    // take lane 0's value so all gates divide by one number
-    sum = __shfl(sum, 0, 64);
-    if (lane < K) gates[lane] = (float)(p / sum);
-}
-
 // ---------------------------------------------------------------- small T
-// grid: (ceil(E/64), ceil(D/64)), block 256.  Thread (rg = tid/16, c = tid%16)
-// handles experts e0 + 4c .. +3 for rows d0 + rg + 16 i, i < 4.
+// grid ceil(E/2), block 256: workgroup w computes the full logits of experts
+// 2w and 2w+1 for every token.  Wave v covers expert 2w + (v & 1) and half
+// (v >> 1) of the d range; lane l owns 16 consecutive d of that half (an
+// expert row is contiguous in the expert-major router layout).
 template <int T>
-__global__ __launch_bounds__(256) void route_small_kernel(moe_router_t r, const void* __restrict__ x,
-                                                          int x_bf16, int32_t* __restrict__ ids,
-                                                          float* __restrict__ gates,
-                                                          double* __restrict__ zpart,
-                                                          double* __restrict__ zfull,
-                                                          int* __restrict__ counters) {
+__global__ __launch_bounds__(256) void route_logits_kernel(moe_router_t r, const void* __restrict__ x, int x_bf16,
+                                                           double* __restrict__ z) {
     const int E = r.n_experts, D = r.d_model;
-    const int ec = blockIdx.x, dc = blockIdx.y;
-    const int ndc = gridDim.y, nec = gridDim.x;
-    const int e0 = ec * kRouteSmallE, d0 = dc * kRouteSmallD;
-    const int tid = threadIdx.x;
-    const int rg = tid >> 4, c = tid & 15;
-
-    __shared__ double xs[T][kRouteSmallD];
-    __shared__ double red[4][T][kRouteSmallE];
-    __shared__ int s_last;
-
-    // issue the weight loads first (16 KB per workgroup, 4 x 16 B per thread)
-    float4 wv[4];
-    const bool full_e = (e0 + kRouteSmallE <= E) && (E % 4 == 0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = blockIdx.x * 2 + (wave & 1);
+    const int half = wave >> 1;
+    const int dh = D / 2;                        // D is a multiple of 32
+    __shared__ double red[2][2][T];
+    double acc[T];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int d = d0 + rg + 16 * i;
-        if (d < D && full_e) {
-            wv[i] = *reinterpret_cast<const float4*>(r.w + (size_t)d * E + e0 + 4 * c);
-        } else {
-            float t4[4];
-            for (int q = 0; q < 4; ++q) {
-                const int e = e0 + 4 * c + q;
-                t4[q] = (d < D && e < E) ? r.w[(size_t)d * E + e] : 0.0f;
+    for (int t = 0; t < T; ++t) acc[t] = 0.0;
+    if (e < E) {
+        const float* wr = r.w + (size_t)e * D + half * dh;
+        for (int d0 = 16 * lane; d0 < dh; d0 += 16 * 64) {
+            float4 wv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wv[q] = *reinterpret_cast<const float4*>(wr + d0 + 4 * q);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const size_t xo = (size_t)t * D + half * dh + d0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[t] = fma(load_x(x, x_bf16, xo + 4 * q), (double)wv[q].x, acc[t]);
+                    acc[t] = fma(load_x(x, x_bf16, xo + 4 * q + 1), (double)wv[q].y, acc[t]);
+                    acc[t] = fma(load_x(x, x_bf16, xo + 4 * q + 2), (double)wv[q].z, acc[t]);
+                    acc[t] = fma(load_x(x, x_bf16, xo + 4 * q + 3), (double)wv[q].w, acc[t]);
+                }
             }
-            wv[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
         }
     }
-    for (int i = tid; i < T * kRouteSmallD; i += 256) {
-        const int t = i / kRouteSmallD, dd = i % kRouteSmallD;
-        const int d = d0 + dd;
-        xs[t][dd] = d < D ? load_x(x, x_bf16, (size_t)t * D + d) : 0.0;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        double v = acc[t];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) red[wave & 1][half][t] = v;
     }
     __syncthreads();
-
-    double acc[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[t][q] = 0.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const double w4[4] = {(double)wv[i].x, (double)wv[i].y, (double)wv[i].z, (double)wv[i].w};
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const double xv = xs[t][rg + 16 * i];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][q] = fma(xv, w4[q], acc[t][q]);
+    if (tid < 2 * T) {
+        const int ee = blockIdx.x * 2 + (tid & 1), t = tid >> 1;
+        if (ee < E) {
+            double s = red[tid & 1][0][t] + red[tid & 1][1][t];
+            if (r.bias) s += (double)r.bias[ee];
+            z[(size_t)t * E + ee] = s;
         }
     }
-    // reduce the 4 row groups of a wavefront (lanes 16 apart), then the 4 waves
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            double v = acc[t][q];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[t][q] = v;
-        }
-    const int wave = tid >> 6;
-    if ((tid & 63) < 16) {
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) red[wave][t][4 * c + q] = acc[t][q];
-    }
-    __syncthreads();
-    for (int i = tid; i < T * kRouteSmallE; i += 256) {
-        const int t = i / kRouteSmallE, ee = i % kRouteSmallE;
-        if (e0 + ee >= E) continue;
-        const double sum = ((red[0][t][ee] + red[1][t][ee]) + red[2][t][ee]) + red[3][t][ee];
-        zpart[((size_t)dc * T + t) * E + e0 + ee] = sum;
-    }
-
-    // last d-chunk of this expert column reduces the partials in d order
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counters[ec], 1) == ndc - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int i = tid; i < T * kRouteSmallE; i += 256) {
-        const int t = i / kRouteSmallE, e = e0 + i % kRouteSmallE;
-        if (e >= E) continue;
-        double s = 0.0;
-        for (int k = 0; k < ndc; ++k) s += zpart[((size_t)k * T + t) * E + e];
-        if (r.bias) s += (double)r.bias[e];
-        zfull[(size_t)t * E + e] = s;
-    }
-    if (tid == 0) counters[ec] = 0;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counters[nec], 1) == nec - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid == 0) counters[nec] = 0;
-    for (int t = wave; t < T; t += 4)
-        wave_topk(zfull + (size_t)t * E, E, r.top_k, ids + (size_t)t * r.top_k, gates + (size_t)t * r.top_k);
 }
 
 // ---------------------------------------------------------------- large T
@@ -223,9 +111,9 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(moe_router_t r, const v
             xs[dd][t] = (tt < T && d < D) ? load_x(x, x_bf16, (size_t)tt * D + d) : 0.0;
         }
         for (int i = tid; i < kRouteTileD * kRouteTileE; i += 256) {
-            const int dd = i / kRouteTileE, ee = i % kRouteTileE;
+            const int ee = i / kRouteTileD, dd = i % kRouteTileD;
             const int d = d0 + dd, e = e0 + ee;
-            ws_[dd][ee] = (d < D && e < E) ? (double)r.w[(size_t)d * E + e] : 0.0;
+            ws_[dd][ee] = (d < D && e < E) ? (double)r.w[(size_t)e * D + d] : 0.0;
         }
         __syncthreads();
 #pragma unroll 4
@@ -271,20 +159,19 @@ namespace qmoe {
 
 hipError_t launch_route_small(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
                               float* gates, char* ws, const RouteWs& L, hipStream_t s) {
-    dim3 grid(cdiv(r.n_experts, kRouteSmallE), cdiv(r.d_model, kRouteSmallD));
-    double* zpart = (double*)(ws + L.zpart);
-    double* zfull = (double*)(ws + L.zfull);
-    int* counters = (int*)(ws + L.counters);
+    double* z = (double*)(ws + L.zfull);
+    const unsigned grid = (unsigned)cdiv(r.n_experts, 2);
     switch (T) {
-#define QMOE_CASE(N)                                                                                       \
-    case N:                                                                                                \
-        route_small_kernel<N><<<grid, 256, 0, s>>>(r, x, x_bf16, ids, gates, zpart, zfull, counters); \
+#define QMOE_CASE(N)                                                         \
+    case N:                                                                  \
+        route_logits_kernel<N><<<grid, 256, 0, s>>>(r, x, x_bf16, z); \
         break;
         QMOE_CASE(1) QMOE_CASE(2) QMOE_CASE(3) QMOE_CASE(4) QMOE_CASE(5) QMOE_CASE(6) QMOE_CASE(7) QMOE_CASE(8)
 #undef QMOE_CASE
         default:
             return hipErrorInvalidValue;
     }
+    topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(z, T, r.n_experts, r.top_k, ids, gates);
     return hipGetLastError();
 }
 

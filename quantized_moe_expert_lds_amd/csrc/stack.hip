@@ -1,0 +1,906 @@
+// Whole decode (or verify) step over a stack of MoE layers in one persistent
+// kernel launch.
+//
+// Each token visits all layers of the model in order (bnskd "Strata：把 125B 大
+// 模型塞进 12GB 显卡", section 投机解码: one forward pass runs all 48 layers; each
+// token is sent to 10 experts, section 核心思路).  At batch 1 a layer moves
+// ~15 MB, about 2 us of HBM time on MI355X, while a kernel launch with 256
+// workgroups costs ~3-4 us and a dependent launch in a graph ~1.6 us, so a
+// step is one cooperative launch with one workgroup per CU that stays
+// resident for all layers; grid barriers replace kernel boundaries.
+//
+// Per layer l, three phases separated by grid barriers:
+//   ROUTE : u_l = h_l (l = 0) or RMSNorm(h_l), computed redundantly by every
+//           workgroup from the residual slices and sums of squares the
+//           workgroups published; workgroup w then computes the fp64 logits
+//           of experts w*EPW .. from router rows it loaded during the previous
+//           layer.
+//   FFN   : every workgroup reads all logits, selects the top-k per token
+//           (ties to the lower id), derives the distinct experts of the batch
+//           and processes its share of (expert, 16-row d_ff chunk) items:
+//           2-/3-bit unpack, fp16 dot products with fp32 accumulation,
+//           SwiGLU, fp16 h per (token, slot) pair.  It also starts loading the
+//           down-projection rows it will need next.
+//   DOWN  : workgroup w owns d_model rows w*DPW ..; it combines those rows of
+//           every distinct expert (blocks in order, slots in order with their
+//           gates), adds the residual and publishes its slice of h and its
+//           sum of squares.
+//
+// Coherence.  Every buffer shared between workgroups exists once per layer,
+// so it is written once per launch, and every 128-byte line of it is written
+// by a single workgroup.  Writers use agent-scope (write-through) stores;
+// after a barrier readers use ordinary cached vector loads: a line can only
+// enter an L2 after its writer finished it, and kernel boundaries invalidate
+// the L2s.  A barrier is a relaxed agent-scope atomic add on one of 8
+// counters (one per XCD slot, 256 B apart) after each thread's stores have
+// completed, and a poll of the 8 counters by 8 lanes.  Every wait is bounded
+// by a wall-clock timeout: on expiry the kernel records an error flag and
+// exits instead of hanging.
+#include "common.hpp"
+
+namespace {
+
+using namespace qmoe;
+using namespace qmoe_dev;
+
+constexpr int kThreads = 256;
+constexpr int kMaxEPW = 4;             // router experts per workgroup
+constexpr int kLine = 64;              // ints between barrier counters (256 B)
+constexpr long long kTimeoutTicks = 400000000LL;   // 4 s of the 100 MHz wall clock
+constexpr int kZW = 16;                // doubles per (workgroup, token) logit line
+constexpr int kHW = 32;                // floats per (workgroup, token) residual line
+constexpr int kHBW = 32;               // words per (pair, 16-row chunk) h line
+constexpr int kMaxItemsInFlight = 2;   // gate/up items whose loads are issued together
+
+struct StackParams {
+    moe_stack_t m;
+    const void* x;
+    int x_bf16;
+    int T;
+    float* h_out;
+    int32_t* ids_out;
+    float* gates_out;
+    double eps;
+    int G;
+    int* sync;          // 8 counters (256 B apart), done counter, error flag
+    double* zb;         // [L][G][T][kZW]      logits of the workgroup's experts
+    float* hb;          // [L][G][T][kHW]      residual rows of the workgroup
+    double* sb;         // [L][G][16]          sums of squares per token
+    uint32_t* hp;       // [L][T*K][F/16][kHBW] SwiGLU h, fp16 pairs in unpack order
+    int lds_us, lds_part, lds_misc, lds_pre, lds_wr;
+    int prefetch_down;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Copy `bytes` (a multiple of 16) from global memory to LDS with the
+// direct-to-LDS load: waves w0 .. w0+nw-1 each move 1 KB per instruction.
+// Lanes past the end re-read the chunk start and write up to 1 KB past
+// dst + bytes, so the destination is padded to a multiple of 1 KB.  The data
+// is in LDS once the issuing waves have waited for vmcnt(0).
+__device__ __forceinline__ void dma_to_lds(const void* src, void* dst, int bytes, int w0, int nw) {
+    const int wave = (threadIdx.x >> 6) - w0, lane = threadIdx.x & 63;
+    for (int off = wave * 1024; off < bytes; off += nw * 1024) {
+        const int o = off + lane * 16;
+        const char* g = (const char*)src + (o < bytes ? o : off);
+        __builtin_amdgcn_global_load_lds(g, (lds_void_t*)((char*)dst + off), 16, 0, 0);
+    }
+}
+
+struct LdsCopy {
+    const void* src;
+    void* dst;
+    int bytes;
+};
+
+// ------------------------------------------------------- coherent stores
+__device__ __forceinline__ void st_f32(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_f64(double* p, double v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------- DPP wavefront reductions
+// Fixed-order reductions to lane 63 (row_shr 1, 2, 4, 8 inside each row of
+// 16 lanes, then row_bcast 15 and 31 across rows), broadcast by readlane.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp0(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_addf(float v) {
+    return v + __int_as_float(dpp0<CTRL, ROWMASK>(__float_as_int(v)));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = dpp_addf<0x111, 0xf>(v);
+    v = dpp_addf<0x112, 0xf>(v);
+    v = dpp_addf<0x114, 0xf>(v);
+    v = dpp_addf<0x118, 0xf>(v);
+    v = dpp_addf<0x142, 0xa>(v);
+    v = dpp_addf<0x143, 0xc>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_addd(double v) {
+    const int lo = dpp0<CTRL, ROWMASK>(__double2loint(v));
+    const int hi = dpp0<CTRL, ROWMASK>(__double2hiint(v));
+    return v + __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = dpp_addd<0x111, 0xf>(v);
+    v = dpp_addd<0x112, 0xf>(v);
+    v = dpp_addd<0x114, 0xf>(v);
+    v = dpp_addd<0x118, 0xf>(v);
+    v = dpp_addd<0x142, 0xa>(v);
+    v = dpp_addd<0x143, 0xc>(v);
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_maxd(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(__double2loint(v), __double2loint(v), CTRL, ROWMASK, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(v), __double2hiint(v), CTRL, ROWMASK, 0xf, false);
+    return fmax(v, __hiloint2double(hi, lo));
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = dpp_maxd<0x111, 0xf>(v);
+    v = dpp_maxd<0x112, 0xf>(v);
+    v = dpp_maxd<0x114, 0xf>(v);
+    v = dpp_maxd<0x118, 0xf>(v);
+    v = dpp_maxd<0x142, 0xa>(v);
+    v = dpp_maxd<0x143, 0xc>(v);
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_mini(int v) {
+    return min(v, __builtin_amdgcn_update_dpp(v, v, CTRL, ROWMASK, 0xf, false));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = dpp_mini<0x111, 0xf>(v);
+    v = dpp_mini<0x112, 0xf>(v);
+    v = dpp_mini<0x114, 0xf>(v);
+    v = dpp_mini<0x118, 0xf>(v);
+    v = dpp_mini<0x142, 0xa>(v);
+    v = dpp_mini<0x143, 0xc>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k of z[0..E) (E <= 64 * kPer) by one wavefront, ranked by (z desc, id
+// asc).  Each lane first sorts its kPer values (ids ascending, so a stable
+// sort on value keeps equal values in id order); each round takes the
+// largest head value over the wavefront (v_max_f64 reductions), the lowest
+// id among heads equal to it (integer min reduction), and pops that head.
+template <int kPer>
+__device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* gates) {
+    const int lane = threadIdx.x & 63;
+    double v[kPer];
+    int id[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? z[e] + 0.0 : -INFINITY;
+        id[i] = e < E ? e : 0x7fffffff;
+    }
+#pragma unroll
+    for (int a = 1; a < kPer; ++a)
+#pragma unroll
+        for (int b = a; b > 0; --b) {
+            const bool sw = v[b] > v[b - 1];
+            const double tv = v[b];
+            const int ti = id[b];
+            v[b] = sw ? v[b - 1] : tv;
+            id[b] = sw ? id[b - 1] : ti;
+            v[b - 1] = sw ? tv : v[b - 1];
+            id[b - 1] = sw ? ti : id[b - 1];
+        }
+    double mine = 0.0;
+    for (int j = 0; j < K; ++j) {
+        const double M = wave_max_f64(v[0]);
+        const int win = wave_min_i32(v[0] == M ? id[0] : 0x7fffffff);
+        if (id[0] == win) {
+#pragma unroll
+            for (int i = 0; i < kPer - 1; ++i) {
+                v[i] = v[i + 1];
+                id[i] = id[i + 1];
+            }
+            v[kPer - 1] = -INFINITY;
+            id[kPer - 1] = 0x7fffffff;
+        }
+        if (lane == j) {
+            mine = M;
+            ids[j] = win;
+        }
+    }
+    const double m0 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(mine), 0),
+                                       __builtin_amdgcn_readlane(__double2loint(mine), 0));
+    const double p = lane < K ? exp(mine - m0) : 0.0;
+    const double sum = wave_sum_f64(p);
+    if (lane < K) gates[lane] = (float)(p / sum);
+}
+
+// Grid barrier number `epoch` (1-based).  Returns false if it timed out or
+// another workgroup reported an error.
+// Waves 1..3 may start an LDS copy (`cp`) while wave 0 waits; it completes
+// by the next barrier.
+__device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, LdsCopy cp = {nullptr, nullptr, 0}) {
+    // every thread waits until its own stores have completed (gfx9 counts
+    // stores in vmcnt; a workgroup-scope release fence emits no wait)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* sync = P.sync;
+    if (threadIdx.x >= 64 && cp.bytes > 0) dma_to_lds(cp.src, cp.dst, cp.bytes, 1, 3);
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        if (lane == 0)
+            __hip_atomic_fetch_add(&sync[(blockIdx.x & 7) * kLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int ok = 1;
+        if (lane < 8) {
+            const int need = epoch * ((P.G - lane + 7) >> 3);
+            const long long t0 = wall_clock64();
+            int n = 0;
+            while (__hip_atomic_load(&sync[lane * kLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                if ((++n & 63) == 0 &&
+                    (__hip_atomic_load(&sync[9 * kLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+                     wall_clock64() - t0 > kTimeoutTicks)) {
+                    ok = 0;
+                    break;
+                }
+            }
+        }
+        const unsigned long long bad = __ballot(lane < 8 && !ok);
+        if (lane == 0) {
+            if (bad) __hip_atomic_store(&sync[9 * kLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_flag = bad ? 0 : 1;
+        }
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// 16 fp16 x pairs in unpack order from 32 fp32 values (LDS)
+__device__ __forceinline__ void pairs_from_f32(const float* v, uint32_t* xp) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        half2_t a = {(_Float16)v[m], (_Float16)v[m + 8]};
+        half2_t b = {(_Float16)v[16 + m], (_Float16)v[24 + m]};
+        xp[m] = as_u32(a);
+        xp[8 + m] = as_u32(b);
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
+    if constexpr (BITS == 2) {
+        const half2_t bias = {(_Float16)-1026.0f, (_Float16)-1026.0f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            lv[m] = as_u32(as_half2(codes2_pair(w[0], 2 * m)) + bias);
+            lv[8 + m] = as_u32(as_half2(codes2_pair(w[1], 2 * m)) + bias);
+        }
+    } else {
+        const half2_t bias = {(_Float16)-1028.0f, (_Float16)-1028.0f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            lv[m] = as_u32(as_half2(codes3_pair(w[0], w[1], w[2], m)) + bias);
+            lv[8 + m] = as_u32(as_half2(codes3_pair(w[0], w[1], w[2], 16 + m)) + bias);
+        }
+    }
+}
+
+__device__ __forceinline__ float dot16h(const uint32_t* lv, const uint32_t* xp) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_fdot2(as_half2(lv[m]), as_half2(xp[m]), acc, false);
+    return acc;
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+template <int W>
+__device__ __forceinline__ void load_block(const uint32_t* qb, size_t blk, uint32_t* q) {
+    if constexpr (W == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(qb + blk * 2);
+        q[0] = v.x;
+        q[1] = v.y;
+    } else {
+        q[0] = qb[blk * 3];
+        q[1] = qb[blk * 3 + 1];
+        q[2] = qb[blk * 3 + 2];
+    }
+}
+
+__host__ __device__ inline int misc_head_bytes(int PT, int T) { return (16 * PT + 2 * PT * T + 15) & ~15; }
+__host__ __device__ inline int hloc_floats(int DPW, int T) {
+    const int a = (DPW > 16 ? DPW : 16) * T;
+    const int b = 16 * T * kMaxItemsInFlight;
+    return a > b ? a : b;
+}
+__host__ __device__ inline int pre_words_per_block(int W) { return W + 1; }   // codes + scale
+
+template <int T, int BITS, int KPER>
+__global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P) {
+    constexpr int W = BITS == 2 ? 2 : 3;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const moe_stack_t& m = P.m;
+    const int L = m.n_layers, E = m.n_experts, D = m.d_model, F = m.d_ff, K = m.top_k;
+    const int G = P.G, w = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nkbD = D >> 5, nkbF = F >> 5, nch = F >> 4;
+    const int PT = T * K;
+    const int EPW = (E + G - 1) / G;
+    const int DPW = (D + G - 1) / G;
+    const int d_lo = min(w * DPW, D), d_hi = min(d_lo + DPW, D);
+    const int nrows = d_hi - d_lo;
+
+    float* us = reinterpret_cast<float*>(lds + P.lds_us);                 // [T][D]
+    float* part = reinterpret_cast<float*>(lds + P.lds_part);             // [PT][DPW][nkbF]
+    double* s_z = reinterpret_cast<double*>(lds + P.lds_part);            // [T][E] (dead before part is used)
+    float* s_z_f = reinterpret_cast<float*>(lds + P.lds_us);              // [PT][DPW] in DOWN (us is dead there)
+    uint32_t* pre = reinterpret_cast<uint32_t*>(lds + P.lds_pre);         // prefetched down blocks
+    unsigned char* misc = lds + P.lds_misc;
+    int* s_ids = reinterpret_cast<int*>(misc);                            // [PT]
+    float* s_gates = reinterpret_cast<float*>(s_ids + PT);                // [PT]
+    int* s_uniq = reinterpret_cast<int*>(s_gates + PT);                   // [PT]
+    int* s_first = s_uniq + PT;                                           // [PT]
+    short* s_upair = reinterpret_cast<short*>(s_first + PT);              // [PT][T]
+    double* s_red = reinterpret_cast<double*>(misc + misc_head_bytes(PT, T));   // [4][kMaxEPW][T]
+    float* s_hloc = reinterpret_cast<float*>(s_red + 4 * kMaxEPW * T);    // see hloc_floats
+    int* s_misc = reinterpret_cast<int*>(s_hloc + hloc_floats(DPW, T));   // [0] = U, [1] = flag
+    double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [T]
+
+    const size_t zb_layer = (size_t)G * T * kZW;
+    const size_t hb_layer = (size_t)G * T * kHW;
+    const size_t sb_layer = (size_t)G * 16;
+    const size_t hp_layer = (size_t)PT * nch * kHBW;
+
+    // router rows of this workgroup's experts live in LDS, copied by DMA one
+    // layer ahead (expert-major rows are contiguous)
+    float* wr_lds = reinterpret_cast<float*>(lds + P.lds_wr);             // [EPW][D]
+    const int e_first = w * EPW;
+    const int my_experts = max(0, min(EPW, E - e_first));
+    auto router_copy = [&](int layer) {
+        return LdsCopy{m.router_w + ((size_t)layer * E + e_first) * D, wr_lds, my_experts * D * 4};
+    };
+    if (my_experts > 0) {
+        const LdsCopy c = router_copy(0);
+        dma_to_lds(c.src, c.dst, c.bytes, 0, 4);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    int epoch = 0;
+    for (int l = 0; l < L; ++l) {
+        // ------------------------------------------------------------- ROUTE
+        if (l == 0) {
+            for (int i = tid; i < T * D; i += kThreads)
+                us[i] = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[i]) : ((const float*)P.x)[i];
+        } else {
+            const double* sbp = P.sb + (size_t)(l - 1) * sb_layer;
+            const float* hbp = P.hb + (size_t)(l - 1) * hb_layer;
+            const int q4 = (DPW + 3) >> 2;            // float4 per slice
+            const int nq = G * T * q4;
+            // issue every load of the phase first
+            float4 hv4[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int i = tid + kThreads * n;
+                if (i < nq) {
+                    const int g = i / (T * q4), rem = i - g * T * q4, t = rem / q4, c = rem - t * q4;
+                    hv4[n] = *reinterpret_cast<const float4*>(hbp + ((size_t)g * T + t) * kHW + 4 * c);
+                }
+            }
+            double ssv[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) ssv[t] = tid < G ? sbp[(size_t)tid * 16 + t] : 0.0;
+            for (int g = tid + kThreads; g < G; g += kThreads)
+#pragma unroll
+                for (int t = 0; t < T; ++t) ssv[t] += sbp[(size_t)g * 16 + t];
+            // sums of squares: fixed order (threads over workgroups, DPP, waves in order)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const double v = wave_sum_f64(ssv[t]);
+                if (lane == 0) s_red[wave * T + t] = v;
+            }
+            __syncthreads();
+            if (tid < T) {
+                const double ss = ((s_red[tid] + s_red[T + tid]) + s_red[2 * T + tid]) + s_red[3 * T + tid];
+                s_r[tid] = sqrt(ss / (double)D + P.eps);
+            }
+            __syncthreads();
+            auto put = [&](int i, const float4& v) {
+                const int g = i / (T * q4), rem = i - g * T * q4, t = rem / q4, c = rem - t * q4;
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+                const double r = s_r[t];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int d = g * DPW + 4 * c + k;
+                    if (4 * c + k < DPW && d < D) us[t * D + d] = (float)((double)vv[k] / r);
+                }
+            };
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int i = tid + kThreads * n;
+                if (i < nq) put(i, hv4[n]);
+            }
+            for (int i = tid + 4 * kThreads; i < nq; i += kThreads) {
+                const int g = i / (T * q4), rem = i - g * T * q4, t = rem / q4, c = rem - t * q4;
+                put(i, *reinterpret_cast<const float4*>(hbp + ((size_t)g * T + t) * kHW + 4 * c));
+            }
+        }
+        __syncthreads();
+        {
+            double acc[kMaxEPW][T];
+#pragma unroll
+            for (int j = 0; j < kMaxEPW; ++j)
+#pragma unroll
+                for (int t = 0; t < T; ++t) acc[j][t] = 0.0;
+            for (int d = tid; d < D; d += kThreads) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const double uv = (double)us[t * D + d];
+#pragma unroll
+                    for (int j = 0; j < kMaxEPW; ++j)
+                        if (j < my_experts) acc[j][t] = fma(uv, (double)wr_lds[j * D + d], acc[j][t]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kMaxEPW; ++j) {
+                if (j >= EPW) break;
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const double v = wave_sum_f64(acc[j][t]);
+                    if (lane == 0) s_red[(wave * kMaxEPW + j) * T + t] = v;
+                }
+            }
+            __syncthreads();
+            if (tid < kMaxEPW * T) {
+                const int j = tid / T, t = tid - j * T;
+                const int e = w * EPW + j;
+                if (j < EPW && e < E) {
+                    double s = ((s_red[(0 * kMaxEPW + j) * T + t] + s_red[(1 * kMaxEPW + j) * T + t]) +
+                                s_red[(2 * kMaxEPW + j) * T + t]) + s_red[(3 * kMaxEPW + j) * T + t];
+                    if (m.router_b) s += (double)m.router_b[(size_t)l * E + e];
+                    st_f64(&P.zb[(size_t)l * zb_layer + ((size_t)w * T + t) * kZW + j], s);
+                }
+            }
+        }
+        // the next layer's router rows stream in while this barrier waits
+        // (every wave is done reading wr_lds once the barrier's entry
+        // __syncthreads has passed)
+        if (!grid_barrier(P, ++epoch, &s_misc[1], l + 1 < L && my_experts > 0 ? router_copy(l + 1) : LdsCopy{nullptr, nullptr, 0}))
+            return;
+
+        // --------------------------------------------------------------- FFN
+        {
+            const double* zbp = P.zb + (size_t)l * zb_layer;
+            for (int i = tid; i < T * E; i += kThreads) {
+                const int t = i / E, e = i - t * E;
+                s_z[i] = zbp[((size_t)(e / EPW) * T + t) * kZW + e % EPW];
+            }
+        }
+        __syncthreads();
+        for (int t = wave; t < T; t += 4) wave_topk_dpp<KPER>(s_z + (size_t)t * E, E, K, s_ids + t * K, s_gates + t * K);
+        __syncthreads();
+        if (w == 0 && P.ids_out) {
+            for (int i = tid; i < PT; i += kThreads) {
+                P.ids_out[(size_t)l * PT + i] = s_ids[i];
+                P.gates_out[(size_t)l * PT + i] = s_gates[i];
+            }
+        }
+        // distinct experts of the batch, in slot order of first appearance
+        if (PT <= 64) {
+            if (wave == 0) {
+                const int e = lane < PT ? s_ids[lane] : -1;
+                int first = lane < PT;
+                for (int q = 0; q < PT; ++q) {
+                    const int eq = __builtin_amdgcn_readlane(e, q);
+                    first &= !(q < lane && eq == e);
+                }
+                const unsigned long long fm = __ballot(first);
+                if (first) {
+                    const int idx = __popcll(fm & ((1ull << lane) - 1ull));
+                    s_uniq[idx] = e;
+                    int pr[T];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) pr[t] = -1;
+                    for (int q = 0; q < PT; ++q)
+                        if (__builtin_amdgcn_readlane(e, q) == e) pr[q / K] = q;
+#pragma unroll
+                    for (int t = 0; t < T; ++t) s_upair[idx * T + t] = (short)pr[t];
+                }
+                if (lane == 0) s_misc[0] = __popcll(fm);
+            }
+        } else {
+            for (int p = tid; p < PT; p += kThreads) {
+                const int e = s_ids[p];
+                int first = 1;
+                for (int q = 0; q < p; ++q) first &= (s_ids[q] != e);
+                s_first[p] = first;
+            }
+            __syncthreads();
+            for (int p = tid; p < PT; p += kThreads) {
+                if (!s_first[p]) continue;
+                int idx = 0;
+                for (int q = 0; q < p; ++q) idx += s_first[q];
+                const int e = s_ids[p];
+                s_uniq[idx] = e;
+                for (int t = 0; t < T; ++t) {
+                    int pr = -1;
+                    for (int j = 0; j < K; ++j)
+                        if (s_ids[t * K + j] == e) pr = t * K + j;
+                    s_upair[idx * T + t] = (short)pr;
+                }
+            }
+            if (tid == 0) {
+                int U = 0;
+                for (int p = 0; p < PT; ++p) U += s_first[p];
+                s_misc[0] = U;
+            }
+        }
+        __syncthreads();
+        const int U = s_misc[0];
+        const size_t lstrideD = (size_t)E * D * nkbF;
+
+        // start loading this workgroup's down-projection rows (used after the
+        // next barrier): thread item (u, kb) -> rows d_lo .. d_hi
+        const bool pref = P.prefetch_down != 0;
+        uint32_t dq[2][8][W];
+        float ds[2][8];
+        if (pref) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int it = tid + kThreads * n;
+                if (it < U * nkbF) {
+                    const int u = it / nkbF, kb = it - u * nkbF;
+                    const int e = s_uniq[u];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        if (r < nrows) {
+                            const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + r) * nkbF + kb;
+                            load_block<W>(m.down_q, blk, dq[n][r]);
+                            ds[n][r] = h2f(m.down_s[blk]);
+                        }
+                    }
+                }
+            }
+        }
+
+        {
+            const int n_items = U * nch;
+            const size_t lstrideGU = (size_t)E * F * nkbD;
+            uint32_t xp0[T][16];                    // x pairs of block kb = lane, built once
+            if (lane < nkbD) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) pairs_from_f32(us + t * D + 32 * lane, xp0[t]);
+            }
+            for (int it0 = w; it0 < n_items; it0 += G * kMaxItemsInFlight) {
+                float acc[kMaxItemsInFlight][8][T];
+                int tmask[kMaxItemsInFlight];       // tokens that chose the item's expert
+#pragma unroll
+                for (int a = 0; a < kMaxItemsInFlight; ++a) {
+                    const int it = it0 + a * G;
+                    int msk = 0;
+                    if (it < n_items) {
+                        const int u = it / nch;
+#pragma unroll
+                        for (int t = 0; t < T; ++t) msk |= (s_upair[u * T + t] >= 0) << t;
+                    }
+                    tmask[a] = __builtin_amdgcn_readfirstlane(msk);
+                }
+#pragma unroll
+                for (int a = 0; a < kMaxItemsInFlight; ++a)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+#pragma unroll
+                        for (int t = 0; t < T; ++t) acc[a][r][t] = 0.0f;
+                for (int kb = lane; kb < nkbD; kb += 64) {
+                    uint32_t q[kMaxItemsInFlight][8][W];
+                    float sc[kMaxItemsInFlight][8];
+#pragma unroll
+                    for (int a = 0; a < kMaxItemsInFlight; ++a) {
+                        const int it = it0 + a * G;
+                        if (it >= n_items) continue;
+                        const int u = it / nch, c = it - u * nch;
+                        const int e = s_uniq[u];
+                        const int f0 = 16 * c + 4 * wave;
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {
+                            const size_t blk = (size_t)l * lstrideGU + ((size_t)e * F + f0 + (r & 3)) * nkbD + kb;
+                            load_block<W>(r < 4 ? m.gate_q : m.up_q, blk, q[a][r]);
+                            sc[a][r] = h2f((r < 4 ? m.gate_s : m.up_s)[blk]);
+                        }
+                    }
+                    uint32_t xpk[T][16];
+                    if (kb >= 64) {
+#pragma unroll
+                        for (int t = 0; t < T; ++t) pairs_from_f32(us + t * D + 32 * kb, xpk[t]);
+                    }
+#pragma unroll
+                    for (int a = 0; a < kMaxItemsInFlight; ++a) {
+                        if (it0 + a * G >= n_items) continue;
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {
+                            uint32_t lv[16];
+                            levels16<BITS>(q[a][r], lv);
+#pragma unroll
+                            for (int t = 0; t < T; ++t)
+                                if ((tmask[a] >> t) & 1)
+                                    acc[a][r][t] = fmaf(sc[a][r], dot16h(lv, kb < 64 ? xp0[t] : xpk[t]), acc[a][r][t]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < kMaxItemsInFlight; ++a) {
+                    const int it = it0 + a * G;
+                    if (it >= n_items) continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int t = 0; t < T; ++t) {
+                            if (!((tmask[a] >> t) & 1)) continue;
+                            const float g = wave_sum_f32(acc[a][r][t]);
+                            const float uu = wave_sum_f32(acc[a][4 + r][t]);
+                            if (lane == 0) s_hloc[(a * T + t) * 16 + 4 * wave + r] = silu_mul(g, uu);
+                        }
+                }
+                __syncthreads();
+                if (tid < 8 * T * kMaxItemsInFlight) {
+                    const int a = tid / (8 * T), rem = tid - a * 8 * T, t = rem >> 3, mm = rem & 7;
+                    const int it = it0 + a * G;
+                    if (it < n_items) {
+                        const int u = it / nch, c = it - u * nch;
+                        const int pr = s_upair[u * T + t];
+                        if (pr >= 0) {
+                            half2_t hv = {(_Float16)s_hloc[(a * T + t) * 16 + mm], (_Float16)s_hloc[(a * T + t) * 16 + mm + 8]};
+                            st_u32(&P.hp[(size_t)l * hp_layer + ((size_t)pr * nch + c) * kHBW + mm], as_u32(hv));
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (pref) {
+            // park the prefetched down blocks in LDS: [item][row][W codes + scale]
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int it = tid + kThreads * n;
+                if (it < U * nkbF) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        if (r < nrows) {
+                            uint32_t* dst = pre + ((size_t)it * DPW + r) * (W + 1);
+#pragma unroll
+                            for (int k = 0; k < W; ++k) dst[k] = dq[n][r][k];
+                            dst[W] = __float_as_uint(ds[n][r]);
+                        }
+                    }
+                }
+            }
+        }
+        if (!grid_barrier(P, ++epoch, &s_misc[1])) return;
+
+        // -------------------------------------------------------------- DOWN
+        {
+            const uint32_t* hpp = P.hp + (size_t)l * hp_layer;
+            for (int it = tid; it < U * nkbF; it += kThreads) {
+                const int u = it / nkbF, kb = it - u * nkbF;
+                const int e = s_uniq[u];
+                uint32_t hv[T][16];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int pr = s_upair[u * T + t];
+                    if (pr < 0) continue;
+                    // block kb of d_ff = 16-row chunks 2kb (pairs 0..7) and 2kb+1 (pairs 8..15)
+                    const uint4* s0 = reinterpret_cast<const uint4*>(hpp + ((size_t)pr * nch + 2 * kb) * kHBW);
+                    const uint4* s1 = reinterpret_cast<const uint4*>(hpp + ((size_t)pr * nch + 2 * kb + 1) * kHBW);
+                    const uint4 a0 = s0[0], a1 = s0[1], b0 = s1[0], b1 = s1[1];
+                    hv[t][0] = a0.x; hv[t][1] = a0.y; hv[t][2] = a0.z; hv[t][3] = a0.w;
+                    hv[t][4] = a1.x; hv[t][5] = a1.y; hv[t][6] = a1.z; hv[t][7] = a1.w;
+                    hv[t][8] = b0.x; hv[t][9] = b0.y; hv[t][10] = b0.z; hv[t][11] = b0.w;
+                    hv[t][12] = b1.x; hv[t][13] = b1.y; hv[t][14] = b1.z; hv[t][15] = b1.w;
+                }
+                for (int r0 = 0; r0 < nrows; r0 += 8) {
+                    uint32_t q[8][W];
+                    float sc[8];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        if (r0 + r >= nrows) continue;
+                        if (pref) {
+                            const uint32_t* src = pre + ((size_t)it * DPW + r0 + r) * (W + 1);
+#pragma unroll
+                            for (int k = 0; k < W; ++k) q[r][k] = src[k];
+                            sc[r] = __uint_as_float(src[W]);
+                        } else {
+                            const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + r0 + r) * nkbF + kb;
+                            load_block<W>(m.down_q, blk, q[r]);
+                            sc[r] = h2f(m.down_s[blk]);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        if (r0 + r >= nrows) continue;
+                        uint32_t lv[16];
+                        levels16<BITS>(q[r], lv);
+#pragma unroll
+                        for (int t = 0; t < T; ++t) {
+                            const int pr = s_upair[u * T + t];
+                            if (pr < 0) continue;
+                            part[((size_t)pr * DPW + r0 + r) * nkbF + kb] = sc[r] * dot16h(lv, hv[t]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            // o[p][r] = sum of blocks in order, one thread per (pair, row)
+            float* s_o = s_z_f;                                          // [PT][DPW], reuses the logit area
+            for (int o = tid; o < PT * nrows; o += kThreads) {
+                const int p = o / nrows, r = o - p * nrows;
+                const float* pp = part + ((size_t)p * DPW + r) * nkbF;
+                float oj = 0.0f;
+                for (int kb = 0; kb < nkbF; ++kb) oj += pp[kb];
+                s_o[p * DPW + r] = oj;
+            }
+            __syncthreads();
+            // y rows (slots in order with their gates), residual, sums of squares
+            for (int o = tid; o < T * nrows; o += kThreads) {
+                const int t = o / nrows, r = o - t * nrows;
+                float yv = 0.0f;
+                for (int j = 0; j < K; ++j) yv = yv + s_gates[t * K + j] * s_o[(t * K + j) * DPW + r];
+                const int d = d_lo + r;
+                float h0;
+                if (l == 0) {
+                    const size_t xi = (size_t)t * D + d;
+                    h0 = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[xi]) : ((const float*)P.x)[xi];
+                } else {
+                    h0 = P.hb[(size_t)(l - 1) * hb_layer + ((size_t)w * T + t) * kHW + r];
+                }
+                const float hn = h0 + yv;
+                if (l + 1 < L) st_f32(&P.hb[(size_t)l * hb_layer + ((size_t)w * T + t) * kHW + r], hn);
+                else P.h_out[(size_t)t * D + d] = hn;
+                s_hloc[t * nrows + r] = hn;
+            }
+            __syncthreads();
+            if (l + 1 < L && tid < T) {
+                double ss = 0.0;
+                for (int r = 0; r < nrows; ++r) {
+                    const double v = (double)s_hloc[tid * nrows + r];
+                    ss += v * v;
+                }
+                st_f64(&P.sb[(size_t)l * sb_layer + (size_t)w * 16 + tid], ss);
+            }
+        }
+        if (l + 1 < L) {
+            if (!grid_barrier(P, ++epoch, &s_misc[1])) return;
+        }
+    }
+    // last arrival resets the counters for the next launch
+    __syncthreads();
+    if (tid == 0) {
+        const int prev = __hip_atomic_fetch_add(&P.sync[8 * kLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == G - 1) {
+            for (int x = 0; x < 9; ++x)
+                __hip_atomic_store(&P.sync[x * kLine], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int T, int BITS, int KPER>
+hipError_t launch_stack_t(StackParams& P, size_t lds, hipStream_t s) {
+    auto fn = decode_stack_kernel<T, BITS, KPER>;
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    void* args[] = {&P};
+    return hipLaunchCooperativeKernel((const void*)fn, dim3(P.G), dim3(kThreads), args, (unsigned)lds, s);
+}
+
+template <int T, int BITS>
+hipError_t launch_stack_e(StackParams& P, size_t lds, hipStream_t s) {
+    const int E = P.m.n_experts;
+    if (E <= 128) return launch_stack_t<T, BITS, 2>(P, lds, s);
+    if (E <= 512) return launch_stack_t<T, BITS, 8>(P, lds, s);
+    return launch_stack_t<T, BITS, 16>(P, lds, s);
+}
+
+}  // namespace
+
+namespace qmoe {
+
+StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L) {
+    StackWs w{};
+    size_t off = 0;
+    w.sync = off;
+    off += align256(sizeof(int) * 10 * kLine);
+    w.zbuf = off;
+    off += align256(sizeof(double) * (size_t)L * G * T * kZW);
+    w.hres = off;
+    off += align256(sizeof(float) * (size_t)L * G * T * kHW);
+    w.ssp = off;
+    off += align256(sizeof(double) * (size_t)L * G * 16);
+    w.hbuf = off;
+    off += align256(sizeof(uint32_t) * (size_t)L * T * K * (F / 16) * kHBW);
+    w.total = off;
+    (void)D;
+    (void)E;
+    return w;
+}
+
+// Down-projection rows are prefetched into LDS when every thread holds at
+// most two (expert, block) items of them.
+static bool stack_prefetch(int T, int D, int F, int K, int G) {
+    const int DPW = (D + G - 1) / G;
+    return DPW <= 8 && (size_t)T * K * (F / 32) <= 2 * (size_t)kThreads;
+}
+
+size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits, int* us_off, int* part_off,
+                       int* misc_off, int* pre_off, int* wr_off) {
+    const int DPW = (D + G - 1) / G;
+    const int PT = T * K;
+    const int W = bits == 2 ? 2 : 3;
+    const int EPW = (E + G - 1) / G;
+    size_t off = 0;
+    const size_t us = off;              // u rows; in DOWN the per-pair sums [PT][DPW]
+    const size_t us_floats = (size_t)T * D > (size_t)PT * DPW ? (size_t)T * D : (size_t)PT * DPW;
+    off += align256(sizeof(float) * us_floats);
+    const size_t part = off;
+    const size_t part_bytes = sizeof(float) * (size_t)PT * DPW * (F / 32);
+    const size_t z_bytes = sizeof(double) * (size_t)T * E;
+    off += align256(part_bytes > z_bytes ? part_bytes : z_bytes);
+    const size_t pre = off;
+    if (stack_prefetch(T, D, F, K, G))
+        off += align256(sizeof(uint32_t) * (size_t)PT * (F / 32) * DPW * pre_words_per_block(W));
+    const size_t wr = off;              // router rows, padded for the 1 KB copy granule
+    off += (sizeof(float) * (size_t)EPW * D + 1023) & ~(size_t)1023;
+    const size_t misc = off;
+    size_t mb = (size_t)misc_head_bytes(PT, T);
+    mb += sizeof(double) * 4 * kMaxEPW * T + sizeof(float) * hloc_floats(DPW, T) + 16 + sizeof(double) * T;
+    off += align256(mb);
+    if (us_off) *us_off = (int)us;
+    if (part_off) *part_off = (int)part;
+    if (misc_off) *misc_off = (int)misc;
+    if (pre_off) *pre_off = (int)pre;
+    if (wr_off) *wr_off = (int)wr;
+    return off;
+}
+
+hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, int T, float* h_out,
+                               int32_t* ids_out, float* gates_out, double eps, char* ws, const StackWs& L, int G,
+                               hipStream_t s) {
+    StackParams P{};
+    P.m = m;
+    P.x = x;
+    P.x_bf16 = x_bf16;
+    P.T = T;
+    P.h_out = h_out;
+    P.ids_out = ids_out;
+    P.gates_out = gates_out;
+    P.eps = eps;
+    P.G = G;
+    P.sync = (int*)(ws + L.sync);
+    P.zb = (double*)(ws + L.zbuf);
+    P.hb = (float*)(ws + L.hres);
+    P.sb = (double*)(ws + L.ssp);
+    P.hp = (uint32_t*)(ws + L.hbuf);
+    P.prefetch_down = stack_prefetch(T, m.d_model, m.d_ff, m.top_k, G) ? 1 : 0;
+    const size_t lds = stack_lds_bytes(T, m.d_model, m.d_ff, m.n_experts, m.top_k, G, m.bits, &P.lds_us,
+                                       &P.lds_part, &P.lds_misc, &P.lds_pre, &P.lds_wr);
+#define QMOE_ST(N)                                                                                 \
+    case N:                                                                                        \
+        return m.bits == 2 ? launch_stack_e<N, 2>(P, lds, s) : launch_stack_e<N, 3>(P, lds, s);
+    switch (T) {
+        QMOE_ST(1) QMOE_ST(2) QMOE_ST(3) QMOE_ST(4) QMOE_ST(5) QMOE_ST(6) QMOE_ST(7) QMOE_ST(8)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef QMOE_ST
+}
+
+}  // namespace qmoe

@@ -56,3 +56,19 @@ def device_layers(wl, n_layers=None, bits=None, device="cuda"):
                        q.Experts(ex["gate_q"][l], ex["up_q"][l], ex["down_q"][l],
                                  ex["gate_s"][l], ex["up_s"][l], ex["down_s"][l], bits)))
     return layers, ex, rt
+
+
+def device_stack(wl, bits=None, n_layers=None, device="cuda"):
+    """The whole model of a workload as one Stack (plus the raw tensors)."""
+    import torch
+    import quantized_moe_expert_lds_amd as q
+    import moe_inputs.gpu as g
+    bits = wl.bits if bits is None else bits
+    ex = g.expert_tensors(wl, n_layers, bits, device)
+    rt = g.routers(wl, n_layers, device)
+    rw = torch.stack([w for w, _ in rt]).contiguous()
+    rb = torch.stack([b for _, b in rt]).contiguous() if wl.zipf_bias else None
+    del rt
+    st = q.Stack(rw, rb, ex["gate_q"], ex["up_q"], ex["down_q"], ex["gate_s"], ex["up_s"], ex["down_s"],
+                 bits, wl.top_k)
+    return st, ex, rw, rb

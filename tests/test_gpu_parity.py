@@ -139,7 +139,7 @@ def test_route_ties(q):
     w[:, 21] = w[:, 3]
     x = rng.standard_normal((T, D)).astype(np.float32)
     for wmat in (w, np.zeros_like(w)):
-        router = q.Router(torch.from_numpy(wmat).cuda(), None, K)
+        router = q.Router(torch.from_numpy(np.ascontiguousarray(wmat.T)).cuda(), None, K)
         ids, g, off, prs = gpu_route(q, router, torch.from_numpy(x).cuda())
         ids_o, gates_o, _ = O.route(x, wmat, None, K)
         check_routing(ids, g, off, prs, ids_o, gates_o, E)
@@ -303,7 +303,7 @@ def test_prefill_one_hot_expert_set(q, full1):
     wmat = np.zeros((D, E), np.float32)
     bias = np.full(E, -10.0, np.float32)
     bias[:K] = np.linspace(1.0, 0.1, K, dtype=np.float32)
-    router = q.Router(torch.from_numpy(wmat).cuda(), torch.from_numpy(bias).cuda(), K)
+    router = q.Router(torch.from_numpy(np.ascontiguousarray(wmat.T)).cuda(), torch.from_numpy(bias).cuda(), K)
     x = mi.activations_host(mi.WORKLOADS["prefill_8192"], 300, stream=3)
     xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
     ids, w, off, prs = gpu_route(q, router, xd)

@@ -23,8 +23,12 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from quantized_moe_expert_lds_amd.build import build_all
-        build_all()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_qmoe_build", os.path.join(ROOT, "quantized_moe_expert_lds_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build_all()
     return ctypes.CDLL(LIB)
 
 
