@@ -195,7 +195,7 @@ int moe_decode_stack(const moe_stack_t* m, const void* x, int x_dtype, int n_tok
     if ((st = check_ws(ws, ws_bytes, Lw.total))) return st;
     // router experts and d_model rows per workgroup
     if ((E + G - 1) / G > 4 || (D + G - 1) / G > 32) return MOE_ERR_UNSUPPORTED;
-    if (stack_lds_bytes(n_tokens, D, F, E, K, G, m->bits, nullptr, nullptr, nullptr, nullptr, nullptr) > kStackLdsLimit)
+    if (stack_lds_bytes(n_tokens, D, F, E, K, G, m->bits) > kStackLdsLimit)
         return MOE_ERR_UNSUPPORTED;
     return hip_status(launch_decode_stack(*m, x, xf, n_tokens, h_out, ids_out, gates_out, eps, (char*)ws, Lw, G,
                                           (hipStream_t)stream));

@@ -48,8 +48,7 @@ constexpr int kStackMaxGrid = 1024;      // workspace sized for up to this many 
 constexpr int kStackMaxD = 4096;
 constexpr size_t kStackLdsLimit = 160 * 1024;
 StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L);
-size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits, int* us_off, int* part_off,
-                       int* misc_off, int* pre_off, int* wr_off);
+size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits);
 
 inline RouteWs route_ws_layout(int T, int D, int E, int K) {
     RouteWs w{};

@@ -67,24 +67,36 @@ struct StackParams {
     float* hb;          // [L][G][T][kHW]      residual rows of the workgroup
     double* sb;         // [L][G][16]          sums of squares per token
     uint32_t* hp;       // [L][T*K][F/16][kHBW] SwiGLU h, fp16 pairs in unpack order
-    int lds_us, lds_part, lds_misc, lds_pre, lds_wr;
-    int prefetch_down;
+    int lds_us, lds_part, lds_misc, lds_pre, lds_wr, lds_xh;
+    // down-projection rows prefetched into LDS: up to pre_cap distinct
+    // experts, each [rows][blocks][W] codes (pre_cstride bytes) followed by
+    // [rows][blocks] fp16 scales (pre_sstride bytes); copy granules in bytes
+    int pre_cap, pre_cstride, pre_sstride, pre_cgran, pre_sgran;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Copy `bytes` (a multiple of 16) from global memory to LDS with the
-// direct-to-LDS load: waves w0 .. w0+nw-1 each move 1 KB per instruction.
-// Lanes past the end re-read the chunk start and write up to 1 KB past
-// dst + bytes, so the destination is padded to a multiple of 1 KB.  The data
-// is in LDS once the issuing waves have waited for vmcnt(0).
-__device__ __forceinline__ void dma_to_lds(const void* src, void* dst, int bytes, int w0, int nw) {
-    const int wave = (threadIdx.x >> 6) - w0, lane = threadIdx.x & 63;
-    for (int off = wave * 1024; off < bytes; off += nw * 1024) {
-        const int o = off + lane * 16;
-        const char* g = (const char*)src + (o < bytes ? o : off);
-        __builtin_amdgcn_global_load_lds(g, (lds_void_t*)((char*)dst + off), 16, 0, 0);
+// One direct-to-LDS chunk: lane i copies GRAN bytes from src + off + i*GRAN
+// to dst + off + i*GRAN (LDS address = M0 base + lane id * GRAN); lanes past
+// `bytes` are masked off.  The data is in LDS once the issuing wave has
+// waited for vmcnt(0).
+__device__ __forceinline__ void dma_chunk(const char* src, char* dst, int off, int bytes, int gran) {
+    const int lane = threadIdx.x & 63;
+    if (gran == 16) {
+        if (off + lane * 16 < bytes)
+            __builtin_amdgcn_global_load_lds(src + off + lane * 16, (lds_void_t*)(dst + off), 16, 0, 0);
+    } else {
+        if (off + lane * 4 < bytes)
+            __builtin_amdgcn_global_load_lds(src + off + lane * 4, (lds_void_t*)(dst + off), 4, 0, 0);
     }
+}
+
+// Copy `bytes` (a multiple of 16, 16-byte aligned) to LDS, 1 KB chunks spread
+// over waves w0 .. w0+nw-1.
+__device__ __forceinline__ void dma_to_lds(const void* src, void* dst, int bytes, int w0, int nw) {
+    const int wave = (threadIdx.x >> 6) - w0;
+    for (int off = wave * 1024; off < bytes; off += nw * 1024)
+        dma_chunk((const char*)src, (char*)dst, off, bytes, 16);
 }
 
 struct LdsCopy {
@@ -170,11 +182,39 @@ __device__ __forceinline__ int wave_min_i32(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ unsigned dpp_maxu(unsigned v) {
+    return max(v, (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWMASK, 0xf, false));
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+    v = dpp_maxu<0x111, 0xf>(v);
+    v = dpp_maxu<0x112, 0xf>(v);
+    v = dpp_maxu<0x114, 0xf>(v);
+    v = dpp_maxu<0x118, 0xf>(v);
+    v = dpp_maxu<0x142, 0xa>(v);
+    v = dpp_maxu<0x143, 0xc>(v);
+    return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// High 32 bits of an unsigned key that orders doubles like their values
+// (-0 is normalised to +0 beforehand).
+__device__ __forceinline__ unsigned order_hi(double v) {
+    const unsigned hi = (unsigned)__double2hiint(v);
+    return (hi & 0x80000000u) ? ~hi : (hi | 0x80000000u);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
 // Top-k of z[0..E) (E <= 64 * kPer) by one wavefront, ranked by (z desc, id
-// asc).  Each lane first sorts its kPer values (ids ascending, so a stable
-// sort on value keeps equal values in id order); each round takes the
-// largest head value over the wavefront (v_max_f64 reductions), the lowest
-// id among heads equal to it (integer min reduction), and pops that head.
+// asc), with softmax gates over the k selected logits.  Each lane sorts its
+// kPer values (ids ascending; a stable sort on value keeps equal values in id
+// order), so a lane's head is its best element.  Each round finds the best
+// head: the largest 32-bit order key over the heads (one DPP max per step)
+// decides alone when a single lane holds it; otherwise the fp64 values and
+// then the ids of the tied lanes decide.  The winning lane pops its head.
 template <int kPer>
 __device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* gates) {
     const int lane = threadIdx.x & 63;
@@ -200,9 +240,19 @@ __device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* ga
         }
     double mine = 0.0;
     for (int j = 0; j < K; ++j) {
-        const double M = wave_max_f64(v[0]);
-        const int win = wave_min_i32(v[0] == M ? id[0] : 0x7fffffff);
-        if (id[0] == win) {
+        const unsigned key = order_hi(v[0]);
+        const unsigned mk = wave_max_u32(key);
+        unsigned long long cand = __ballot(key == mk);
+        if (__popcll(cand) > 1) {
+            // tie on the high key bits: exact value, then lowest id
+            const double M = wave_max_f64(key == mk ? v[0] : -INFINITY);
+            const int wid = wave_min_i32(key == mk && v[0] == M ? id[0] : 0x7fffffff);
+            cand = __ballot(key == mk && id[0] == wid);
+        }
+        const int wl = __ffsll((long long)cand) - 1;
+        const double M = readlane_f64(v[0], wl);
+        const int win = __builtin_amdgcn_readlane(id[0], wl);
+        if (lane == wl) {
 #pragma unroll
             for (int i = 0; i < kPer - 1; ++i) {
                 v[i] = v[i + 1];
@@ -216,8 +266,7 @@ __device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* ga
             ids[j] = win;
         }
     }
-    const double m0 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(mine), 0),
-                                       __builtin_amdgcn_readlane(__double2loint(mine), 0));
+    const double m0 = readlane_f64(mine, 0);
     const double p = lane < K ? exp(mine - m0) : 0.0;
     const double sum = wave_sum_f64(p);
     if (lane < K) gates[lane] = (float)(p / sum);
@@ -262,17 +311,6 @@ __device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, LdsCo
     return *s_flag != 0;
 }
 
-// 16 fp16 x pairs in unpack order from 32 fp32 values (LDS)
-__device__ __forceinline__ void pairs_from_f32(const float* v, uint32_t* xp) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        half2_t a = {(_Float16)v[m], (_Float16)v[m + 8]};
-        half2_t b = {(_Float16)v[16 + m], (_Float16)v[24 + m]};
-        xp[m] = as_u32(a);
-        xp[8 + m] = as_u32(b);
-    }
-}
-
 template <int BITS>
 __device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
     if constexpr (BITS == 2) {
@@ -301,6 +339,15 @@ __device__ __forceinline__ float dot16h(const uint32_t* lv, const uint32_t* xp) 
 
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// u as fp16 in unpack order, one 17-word row per 32-element block (16 pair
+// words + 1 pad word, so lane-per-block reads hit distinct banks).  Element
+// i of a block sits in pair word (i & 16) / 2 + (i & 7), half (i >> 3) & 1.
+constexpr int kXhWords = 17;
+__device__ __forceinline__ int xh_half_index(int t, int nkb, int d) {
+    const int kb = d >> 5, i = d & 31;
+    return ((t * nkb + kb) * kXhWords + ((i >> 4) << 3) + (i & 7)) * 2 + ((i >> 3) & 1);
+}
+
 template <int W>
 __device__ __forceinline__ void load_block(const uint32_t* qb, size_t blk, uint32_t* q) {
     if constexpr (W == 2) {
@@ -320,7 +367,6 @@ __host__ __device__ inline int hloc_floats(int DPW, int T) {
     const int b = 16 * T * kMaxItemsInFlight;
     return a > b ? a : b;
 }
-__host__ __device__ inline int pre_words_per_block(int W) { return W + 1; }   // codes + scale
 
 template <int T, int BITS, int KPER>
 __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P) {
@@ -338,6 +384,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     const int nrows = d_hi - d_lo;
 
     float* us = reinterpret_cast<float*>(lds + P.lds_us);                 // [T][D]
+    _Float16* xh = reinterpret_cast<_Float16*>(lds + P.lds_xh);           // [T][D/32][17 words]
+    const uint32_t* xhw = reinterpret_cast<const uint32_t*>(lds + P.lds_xh);
     float* part = reinterpret_cast<float*>(lds + P.lds_part);             // [PT][DPW][nkbF]
     double* s_z = reinterpret_cast<double*>(lds + P.lds_part);            // [T][E] (dead before part is used)
     float* s_z_f = reinterpret_cast<float*>(lds + P.lds_us);              // [PT][DPW] in DOWN (us is dead there)
@@ -352,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     float* s_hloc = reinterpret_cast<float*>(s_red + 4 * kMaxEPW * T);    // see hloc_floats
     int* s_misc = reinterpret_cast<int*>(s_hloc + hloc_floats(DPW, T));   // [0] = U, [1] = flag
     double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [T]
+    float* s_hres = reinterpret_cast<float*>(s_r + T);                    // [T][DPW] own residual rows
 
     const size_t zb_layer = (size_t)G * T * kZW;
     const size_t hb_layer = (size_t)G * T * kHW;
@@ -370,15 +419,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         const LdsCopy c = router_copy(0);
         dma_to_lds(c.src, c.dst, c.bytes, 0, 4);
     }
+    for (int i = tid; i < T * nrows; i += kThreads) {
+        const int t = i / nrows, r = i - t * nrows;
+        const size_t xi = (size_t)t * D + d_lo + r;
+        s_hres[t * DPW + r] = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[xi]) : ((const float*)P.x)[xi];
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     int epoch = 0;
     for (int l = 0; l < L; ++l) {
         // ------------------------------------------------------------- ROUTE
+        float bias_v = 0.0f;           // bias of (expert j, token t) for thread j*T + t
+        if (m.router_b && tid < kMaxEPW * T) {
+            const int j = tid / T, e = w * EPW + j;
+            if (j < EPW && e < E) bias_v = m.router_b[(size_t)l * E + e];
+        }
         if (l == 0) {
             for (int i = tid; i < T * D; i += kThreads)
-                us[i] = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[i]) : ((const float*)P.x)[i];
+            {
+                const float v = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[i]) : ((const float*)P.x)[i];
+                us[i] = v;
+                xh[xh_half_index(i / D, nkbD, i % D)] = (_Float16)v;
+            }
         } else {
             const double* sbp = P.sb + (size_t)(l - 1) * sb_layer;
             const float* hbp = P.hb + (size_t)(l - 1) * hb_layer;
@@ -419,7 +482,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int d = g * DPW + 4 * c + k;
-                    if (4 * c + k < DPW && d < D) us[t * D + d] = (float)((double)vv[k] / r);
+                    if (4 * c + k < DPW && d < D) {
+                        const float uv = (float)((double)vv[k] / r);
+                        us[t * D + d] = uv;
+                        xh[xh_half_index(t, nkbD, d)] = (_Float16)uv;
+                    }
                 }
             };
 #pragma unroll
@@ -464,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 if (j < EPW && e < E) {
                     double s = ((s_red[(0 * kMaxEPW + j) * T + t] + s_red[(1 * kMaxEPW + j) * T + t]) +
                                 s_red[(2 * kMaxEPW + j) * T + t]) + s_red[(3 * kMaxEPW + j) * T + t];
-                    if (m.router_b) s += (double)m.router_b[(size_t)l * E + e];
+                    s += (double)bias_v;
                     st_f64(&P.zb[(size_t)l * zb_layer + ((size_t)w * T + t) * kZW + j], s);
                 }
             }
@@ -477,10 +544,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
 
         // --------------------------------------------------------------- FFN
         {
+            // logit lines (workgroup g, token t), all loads of a round in flight
             const double* zbp = P.zb + (size_t)l * zb_layer;
-            for (int i = tid; i < T * E; i += kThreads) {
-                const int t = i / E, e = i - t * E;
-                s_z[i] = zbp[((size_t)(e / EPW) * T + t) * kZW + e % EPW];
+            const int nz = G * T;
+            for (int i0 = 0; i0 < nz; i0 += 4 * kThreads) {
+                double2 v[4][2];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int i = min(i0 + tid + a * kThreads, nz - 1);
+                    const double2* src = reinterpret_cast<const double2*>(zbp + (size_t)i * kZW);
+                    v[a][0] = src[0];
+                    v[a][1] = src[1];
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int i = i0 + tid + a * kThreads;
+                    if (i < nz) {
+                        const int g = i / T, t = i - g * T;
+                        const double vv[4] = {v[a][0].x, v[a][0].y, v[a][1].x, v[a][1].y};
+#pragma unroll
+                        for (int j = 0; j < kMaxEPW; ++j) {
+                            const int e = g * EPW + j;
+                            if (j < EPW && e < E) s_z[t * E + e] = vv[j];
+                        }
+                    }
+                }
             }
         }
         __syncthreads();
@@ -544,53 +632,60 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         }
         __syncthreads();
         const int U = s_misc[0];
-        const size_t lstrideD = (size_t)E * D * nkbF;
 
-        // start loading this workgroup's down-projection rows (used after the
-        // next barrier): thread item (u, kb) -> rows d_lo .. d_hi
-        const bool pref = P.prefetch_down != 0;
-        uint32_t dq[2][8][W];
-        float ds[2][8];
-        if (pref) {
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int it = tid + kThreads * n;
-                if (it < U * nkbF) {
-                    const int u = it / nkbF, kb = it - u * nkbF;
-                    const int e = s_uniq[u];
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        if (r < nrows) {
-                            const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + r) * nkbF + kb;
-                            load_block<W>(m.down_q, blk, dq[n][r]);
-                            ds[n][r] = h2f(m.down_s[blk]);
-                        }
-                    }
-                }
+        const size_t lstrideD = (size_t)E * D * nkbF;
+        // Copies into LDS make the compiler wait for them before any later
+        // LDS access, so everything this phase reads from LDS before its
+        // weight loads is read first, and the copies are issued right after
+        // those loads.
+        const int uid = lane < U ? s_uniq[lane] : 0;     // distinct expert `lane` (first 64)
+        const int n_pre = min(U, P.pre_cap);
+        // copy this workgroup's down-projection rows d_lo .. d_hi of the first
+        // n_pre distinct experts into LDS (used after the next barrier);
+        // chunks are dealt to the waves round-robin.  Wave-uniform control
+        // flow only: every lane of the wave takes part in a chunk.
+        auto issue_down_prefetch = [&]() {
+            if (nrows <= 0) return;
+            const int cbytes = nrows * nkbF * W * 4, sbytes = nrows * nkbF * 2;
+            int ci = 0;
+            for (int u = 0; u < n_pre; ++u) {
+                const int e = u < 64 ? __builtin_amdgcn_readlane(uid, u) : s_uniq[u];
+                const size_t row0 = ((size_t)l * E + e) * D + d_lo;
+                const char* csrc = reinterpret_cast<const char*>(m.down_q + row0 * nkbF * W);
+                const char* ssrc = reinterpret_cast<const char*>(m.down_s + row0 * nkbF);
+                char* cdst = reinterpret_cast<char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
+                for (int off = 0; off < cbytes; off += 64 * P.pre_cgran, ++ci)
+                    if ((ci & 3) == wave) dma_chunk(csrc, cdst, off, cbytes, P.pre_cgran);
+                for (int off = 0; off < sbytes; off += 64 * P.pre_sgran, ++ci)
+                    if ((ci & 3) == wave) dma_chunk(ssrc, cdst + P.pre_cstride, off, sbytes, P.pre_sgran);
             }
-        }
+        };
+        bool prefetch_pending = true;
 
         {
             const int n_items = U * nch;
             const size_t lstrideGU = (size_t)E * F * nkbD;
-            uint32_t xp0[T][16];                    // x pairs of block kb = lane, built once
-            if (lane < nkbD) {
+            uint32_t xp0[T][16];                    // x pairs of block kb = lane (clamped), read once
 #pragma unroll
-                for (int t = 0; t < T; ++t) pairs_from_f32(us + t * D + 32 * lane, xp0[t]);
-            }
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int mm = 0; mm < 16; ++mm) xp0[t][mm] = xhw[(t * nkbD + min(lane, nkbD - 1)) * kXhWords + mm];
             for (int it0 = w; it0 < n_items; it0 += G * kMaxItemsInFlight) {
                 float acc[kMaxItemsInFlight][8][T];
                 int tmask[kMaxItemsInFlight];       // tokens that chose the item's expert
+                int ie[kMaxItemsInFlight];          // the item's expert
 #pragma unroll
                 for (int a = 0; a < kMaxItemsInFlight; ++a) {
                     const int it = it0 + a * G;
-                    int msk = 0;
+                    int msk = 0, e = 0;
                     if (it < n_items) {
                         const int u = it / nch;
 #pragma unroll
                         for (int t = 0; t < T; ++t) msk |= (s_upair[u * T + t] >= 0) << t;
+                        e = s_uniq[u];
                     }
                     tmask[a] = __builtin_amdgcn_readfirstlane(msk);
+                    ie[a] = __builtin_amdgcn_readfirstlane(e);
                 }
 #pragma unroll
                 for (int a = 0; a < kMaxItemsInFlight; ++a)
@@ -598,28 +693,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     for (int r = 0; r < 8; ++r)
 #pragma unroll
                         for (int t = 0; t < T; ++t) acc[a][r][t] = 0.0f;
-                for (int kb = lane; kb < nkbD; kb += 64) {
+                for (int kb0 = 0; kb0 < nkbD; kb0 += 64) {        // wave-uniform loop
+                    const int kb = kb0 + lane;
+                    const bool kact = kb < nkbD;
+                    const int kbc = kact ? kb : nkbD - 1;         // loads stay in bounds
                     uint32_t q[kMaxItemsInFlight][8][W];
-                    float sc[kMaxItemsInFlight][8];
+                    uint16_t sr[kMaxItemsInFlight][8];
 #pragma unroll
                     for (int a = 0; a < kMaxItemsInFlight; ++a) {
                         const int it = it0 + a * G;
                         if (it >= n_items) continue;
-                        const int u = it / nch, c = it - u * nch;
-                        const int e = s_uniq[u];
+                        const int c = it - (it / nch) * nch;
                         const int f0 = 16 * c + 4 * wave;
 #pragma unroll
                         for (int r = 0; r < 8; ++r) {
-                            const size_t blk = (size_t)l * lstrideGU + ((size_t)e * F + f0 + (r & 3)) * nkbD + kb;
+                            const size_t blk = (size_t)l * lstrideGU + ((size_t)ie[a] * F + f0 + (r & 3)) * nkbD + kbc;
                             load_block<W>(r < 4 ? m.gate_q : m.up_q, blk, q[a][r]);
-                            sc[a][r] = h2f((r < 4 ? m.gate_s : m.up_s)[blk]);
+                            sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
                         }
                     }
-                    uint32_t xpk[T][16];
-                    if (kb >= 64) {
-#pragma unroll
-                        for (int t = 0; t < T; ++t) pairs_from_f32(us + t * D + 32 * kb, xpk[t]);
+                    if (prefetch_pending) {
+                        prefetch_pending = false;
+                        issue_down_prefetch();
                     }
+                    uint32_t xpk[T][16];
+                    if (kb0 > 0) {
+#pragma unroll
+                        for (int t = 0; t < T; ++t)
+#pragma unroll
+                            for (int mm = 0; mm < 16; ++mm) xpk[t][mm] = xhw[(t * nkbD + kbc) * kXhWords + mm];
+                    }
+                    // every loaded register is consumed on every path (lanes past
+                    // the last block add 0), so no load is left in flight at the
+                    // loop's back edge
 #pragma unroll
                     for (int a = 0; a < kMaxItemsInFlight; ++a) {
                         if (it0 + a * G >= n_items) continue;
@@ -627,10 +733,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         for (int r = 0; r < 8; ++r) {
                             uint32_t lv[16];
                             levels16<BITS>(q[a][r], lv);
+                            const float sc = kact ? h2f(sr[a][r]) : 0.0f;
 #pragma unroll
                             for (int t = 0; t < T; ++t)
                                 if ((tmask[a] >> t) & 1)
-                                    acc[a][r][t] = fmaf(sc[a][r], dot16h(lv, kb < 64 ? xp0[t] : xpk[t]), acc[a][r][t]);
+                                    acc[a][r][t] = fmaf(sc, dot16h(lv, kb0 == 0 ? xp0[t] : xpk[t]), acc[a][r][t]);
                         }
                     }
                 }
@@ -664,24 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 __syncthreads();
             }
         }
-        if (pref) {
-            // park the prefetched down blocks in LDS: [item][row][W codes + scale]
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int it = tid + kThreads * n;
-                if (it < U * nkbF) {
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        if (r < nrows) {
-                            uint32_t* dst = pre + ((size_t)it * DPW + r) * (W + 1);
-#pragma unroll
-                            for (int k = 0; k < W; ++k) dst[k] = dq[n][r][k];
-                            dst[W] = __float_as_uint(ds[n][r]);
-                        }
-                    }
-                }
-            }
-        }
+        if (prefetch_pending) issue_down_prefetch();      // workgroups without gate/up items
         if (!grid_barrier(P, ++epoch, &s_misc[1])) return;
 
         // -------------------------------------------------------------- DOWN
@@ -704,33 +794,50 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     hv[t][8] = b0.x; hv[t][9] = b0.y; hv[t][10] = b0.z; hv[t][11] = b0.w;
                     hv[t][12] = b1.x; hv[t][13] = b1.y; hv[t][14] = b1.z; hv[t][15] = b1.w;
                 }
-                for (int r0 = 0; r0 < nrows; r0 += 8) {
-                    uint32_t q[8][W];
-                    float sc[8];
+                if (u < n_pre) {
+                    // rows from LDS (nrows <= 8 whenever experts are prefetched)
+                    const char* cb = reinterpret_cast<const char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
+                    const uint32_t* cw = reinterpret_cast<const uint32_t*>(cb);
+                    const uint16_t* sw = reinterpret_cast<const uint16_t*>(cb + P.pre_cstride);
 #pragma unroll
                     for (int r = 0; r < 8; ++r) {
-                        if (r0 + r >= nrows) continue;
-                        if (pref) {
-                            const uint32_t* src = pre + ((size_t)it * DPW + r0 + r) * (W + 1);
+                        if (r >= nrows) continue;
+                        uint32_t qv[W];
 #pragma unroll
-                            for (int k = 0; k < W; ++k) q[r][k] = src[k];
-                            sc[r] = __uint_as_float(src[W]);
-                        } else {
-                            const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + r0 + r) * nkbF + kb;
-                            load_block<W>(m.down_q, blk, q[r]);
-                            sc[r] = h2f(m.down_s[blk]);
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        if (r0 + r >= nrows) continue;
+                        for (int k = 0; k < W; ++k) qv[k] = cw[(r * nkbF + kb) * W + k];
+                        const float sc = h2f(sw[r * nkbF + kb]);
                         uint32_t lv[16];
-                        levels16<BITS>(q[r], lv);
+                        levels16<BITS>(qv, lv);
 #pragma unroll
                         for (int t = 0; t < T; ++t) {
                             const int pr = s_upair[u * T + t];
                             if (pr < 0) continue;
-                            part[((size_t)pr * DPW + r0 + r) * nkbF + kb] = sc[r] * dot16h(lv, hv[t]);
+                            part[((size_t)pr * DPW + r) * nkbF + kb] = sc * dot16h(lv, hv[t]);
+                        }
+                    }
+                } else {
+                    for (int r0 = 0; r0 < nrows; r0 += 8) {
+                        uint32_t q[8][W];
+                        uint16_t sr[8];
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {      // clamped rows: every load is issued unconditionally
+                            const int rr = min(r0 + r, nrows - 1);
+                            const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + rr) * nkbF + kb;
+                            load_block<W>(m.down_q, blk, q[r]);
+                            sr[r] = m.down_s[blk];
+                        }
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {
+                            if (r0 + r >= nrows) continue;
+                            uint32_t lv[16];
+                            levels16<BITS>(q[r], lv);
+                            const float sc = h2f(sr[r]);
+#pragma unroll
+                            for (int t = 0; t < T; ++t) {
+                                const int pr = s_upair[u * T + t];
+                                if (pr < 0) continue;
+                                part[((size_t)pr * DPW + r0 + r) * nkbF + kb] = sc * dot16h(lv, hv[t]);
+                            }
                         }
                     }
                 }
@@ -752,14 +859,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 float yv = 0.0f;
                 for (int j = 0; j < K; ++j) yv = yv + s_gates[t * K + j] * s_o[(t * K + j) * DPW + r];
                 const int d = d_lo + r;
-                float h0;
-                if (l == 0) {
-                    const size_t xi = (size_t)t * D + d;
-                    h0 = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[xi]) : ((const float*)P.x)[xi];
-                } else {
-                    h0 = P.hb[(size_t)(l - 1) * hb_layer + ((size_t)w * T + t) * kHW + r];
-                }
-                const float hn = h0 + yv;
+                const float hn = s_hres[t * DPW + r] + yv;
+                s_hres[t * DPW + r] = hn;
                 if (l + 1 < L) st_f32(&P.hb[(size_t)l * hb_layer + ((size_t)w * T + t) * kHW + r], hn);
                 else P.h_out[(size_t)t * D + d] = hn;
                 s_hloc[t * nrows + r] = hn;
@@ -833,42 +934,60 @@ StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L) {
     return w;
 }
 
-// Down-projection rows are prefetched into LDS when every thread holds at
-// most two (expert, block) items of them.
-static bool stack_prefetch(int T, int D, int F, int K, int G) {
-    const int DPW = (D + G - 1) / G;
-    return DPW <= 8 && (size_t)T * K * (F / 32) <= 2 * (size_t)kThreads;
-}
+// LDS plan of one workgroup.  Whatever the fixed regions leave of the LDS
+// limit holds prefetched down-projection rows, whole experts at a time.
+struct StackLds {
+    size_t us, part, wr, xh, misc, pre, total;
+    int pre_cap, cstride, sstride, cgran, sgran;
+};
 
-size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits, int* us_off, int* part_off,
-                       int* misc_off, int* pre_off, int* wr_off) {
+static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bits) {
+    StackLds p{};
     const int DPW = (D + G - 1) / G;
+    const int EPW = (E + G - 1) / G;
     const int PT = T * K;
     const int W = bits == 2 ? 2 : 3;
-    const int EPW = (E + G - 1) / G;
+    const int nkbF = F / 32;
     size_t off = 0;
-    const size_t us = off;              // u rows; in DOWN the per-pair sums [PT][DPW]
+    p.us = off;                        // u rows; in DOWN the per-pair sums [PT][DPW]
     const size_t us_floats = (size_t)T * D > (size_t)PT * DPW ? (size_t)T * D : (size_t)PT * DPW;
     off += align256(sizeof(float) * us_floats);
-    const size_t part = off;
-    const size_t part_bytes = sizeof(float) * (size_t)PT * DPW * (F / 32);
-    const size_t z_bytes = sizeof(double) * (size_t)T * E;
-    off += align256(part_bytes > z_bytes ? part_bytes : z_bytes);
-    const size_t pre = off;
-    if (stack_prefetch(T, D, F, K, G))
-        off += align256(sizeof(uint32_t) * (size_t)PT * (F / 32) * DPW * pre_words_per_block(W));
-    const size_t wr = off;              // router rows, padded for the 1 KB copy granule
-    off += (sizeof(float) * (size_t)EPW * D + 1023) & ~(size_t)1023;
-    const size_t misc = off;
+    // ROUTE and FFN: logits [T][E] doubles, then u in fp16 pair order
+    // (padded); DOWN: per-block partial sums [PT][DPW][F/32] floats
+    p.part = off;
+    const size_t part_bytes = sizeof(float) * (size_t)PT * DPW * nkbF;
+    const size_t z_bytes = align256(sizeof(double) * (size_t)T * E);
+    const size_t xh_bytes = sizeof(uint32_t) * (size_t)T * (D / 32) * kXhWords;
+    p.xh = off + z_bytes;
+    off += align256(part_bytes > z_bytes + xh_bytes ? part_bytes : z_bytes + xh_bytes);
+    p.wr = off;                        // router rows
+    off += align256(sizeof(float) * (size_t)EPW * D);
+    p.misc = off;
     size_t mb = (size_t)misc_head_bytes(PT, T);
-    mb += sizeof(double) * 4 * kMaxEPW * T + sizeof(float) * hloc_floats(DPW, T) + 16 + sizeof(double) * T;
+    mb += sizeof(double) * 4 * kMaxEPW * T + sizeof(float) * hloc_floats(DPW, T) + 16 + sizeof(double) * T +
+          sizeof(float) * (size_t)T * DPW;
     off += align256(mb);
-    if (us_off) *us_off = (int)us;
-    if (part_off) *part_off = (int)part;
-    if (misc_off) *misc_off = (int)misc;
-    if (pre_off) *pre_off = (int)pre;
-    if (wr_off) *wr_off = (int)wr;
-    return off;
+    p.pre = off;
+    p.total = off;
+    // prefetch: at most 8 rows per workgroup; copy granule 16 B where rows of
+    // codes / scales are multiples of 16 B, else 4 B; odd block counts are
+    // not prefetched
+    p.cstride = (int)((sizeof(uint32_t) * (size_t)DPW * nkbF * W + 15) & ~(size_t)15);
+    p.sstride = (int)((sizeof(uint16_t) * (size_t)DPW * nkbF + 15) & ~(size_t)15);
+    p.cgran = (nkbF * W) % 4 == 0 ? 16 : 4;
+    p.sgran = nkbF % 8 == 0 ? 16 : 4;
+    if (DPW <= 8 && nkbF % 2 == 0 && off < (size_t)kStackLdsLimit) {
+        const size_t per = (size_t)p.cstride + p.sstride;
+        size_t cap = ((size_t)kStackLdsLimit - off) / per;
+        if (cap > (size_t)PT) cap = PT;
+        p.pre_cap = (int)cap;
+        p.total = off + cap * per;
+    }
+    return p;
+}
+
+size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits) {
+    return stack_lds_plan(T, D, F, E, K, G, bits).total;
 }
 
 hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, int T, float* h_out,
@@ -889,9 +1008,21 @@ hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, 
     P.hb = (float*)(ws + L.hres);
     P.sb = (double*)(ws + L.ssp);
     P.hp = (uint32_t*)(ws + L.hbuf);
-    P.prefetch_down = stack_prefetch(T, m.d_model, m.d_ff, m.top_k, G) ? 1 : 0;
-    const size_t lds = stack_lds_bytes(T, m.d_model, m.d_ff, m.n_experts, m.top_k, G, m.bits, &P.lds_us,
-                                       &P.lds_part, &P.lds_misc, &P.lds_pre, &P.lds_wr);
+    const StackLds pl = stack_lds_plan(T, m.d_model, m.d_ff, m.n_experts, m.top_k, G, m.bits);
+    P.lds_us = (int)pl.us;
+    P.lds_part = (int)pl.part;
+    P.lds_wr = (int)pl.wr;
+    P.lds_xh = (int)pl.xh;
+    P.lds_misc = (int)pl.misc;
+    P.lds_pre = (int)pl.pre;
+    // prefetch needs 16-byte aligned rows for the 16-byte granule
+    const bool al = ((uintptr_t)m.down_q % 16 == 0) && ((uintptr_t)m.down_s % 16 == 0);
+    P.pre_cap = al ? pl.pre_cap : 0;
+    P.pre_cstride = pl.cstride;
+    P.pre_sstride = pl.sstride;
+    P.pre_cgran = pl.cgran;
+    P.pre_sgran = pl.sgran;
+    const size_t lds = pl.total;
 #define QMOE_ST(N)                                                                                 \
     case N:                                                                                        \
         return m.bits == 2 ? launch_stack_e<N, 2>(P, lds, s) : launch_stack_e<N, 3>(P, lds, s);
