@@ -25,8 +25,8 @@ constexpr int kBucketBlock = 256;
 // prefill grouped GEMM tile
 constexpr int kGemmBM = 128;
 constexpr int kGemmBK = 64;
-constexpr int kGateUpBN = 64;     // d_ff columns per gate/up tile (x2 for gate and up)
-constexpr int kDownBN = 128;      // d_model columns per down tile
+constexpr int kGateUpBN = 128;    // d_ff columns per gate/up tile (x2 for gate and up)
+constexpr int kDownBN = 256;      // d_model columns per down tile
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }

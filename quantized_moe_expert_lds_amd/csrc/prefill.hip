@@ -132,9 +132,81 @@ __device__ __forceinline__ half8_t lds_frag(const _Float16* base) {
     return *reinterpret_cast<const half8_t*>(base);
 }
 
-// ------------------------------------------------------- 3. gate/up GEMM
-// block 256 = 4 waves (wm = wave & 1, wn = wave >> 1); wave tile = 64 rows x
-// (32 gate + 32 up) columns.
+// ---------------------------------------------------- 3./4. grouped GEMMs
+// Both GEMMs: a block of 256 threads (4 waves) computes a 128-row x 256-column
+// tile (rows = pairs of one bucket; columns = 128 d_ff columns of gate plus
+// the same 128 of up, or 256 d_model columns), K in steps of 64 through LDS.
+// Wave w owns rows 64 (w & 1) .. +64 and LDS B rows 128 (w >> 1) .. +128: a
+// 64 x 128 patch of 4 x 8 MFMA 16x16x32 tiles, so each fragment read from
+// LDS feeds 4 or 8 MFMAs.  16-row slices holding no pair of the bucket skip
+// their MFMAs.  B rows are dequantised from 2-bit blocks: thread t owns B
+// row t, both blocks of a step.  The next step's operands are loaded into
+// registers while the current step multiplies.
+struct GemmStage {
+    uint4 a[4];        // A rows (tid >> 3) + 32 i, 16-byte column chunk tid & 7
+    uint4 b;           // codes of the two blocks of B row tid in this step
+    uint32_t s;        // their fp16 scales
+};
+
+__device__ __forceinline__ void gemm_load(GemmStage& st, const uint16_t* const* a_src, const uint32_t* b_q,
+                                          const uint16_t* b_s, int ks) {
+    const int k0 = ks * kGemmBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        st.a[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    st.b = *reinterpret_cast<const uint4*>(b_q + (size_t)ks * 4);
+    st.s = *reinterpret_cast<const uint32_t*>(b_s + (size_t)ks * 2);
+}
+
+__device__ __forceinline__ void gemm_store(const GemmStage& st, _Float16 (*As)[kLdsStride],
+                                           _Float16 (*Bs)[kLdsStride], int b_lds_row) {
+    const int tid = threadIdx.x;
+    const int a_col = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[(tid >> 3) + 32 * i][a_col]) = st.a[i];
+    uint32_t o[16];
+    uint4* dst = reinterpret_cast<uint4*>(&Bs[b_lds_row][0]);
+    dequant_block2(st.b.x, st.b.y, (uint16_t)(st.s & 0xffff), o);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    dequant_block2(st.b.z, st.b.w, (uint16_t)(st.s >> 16), o);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[4 + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+}
+
+// the K loop shared by both GEMMs; ni = 16-row slices of the wave that hold pairs
+__device__ __forceinline__ void gemm_kloop(const uint16_t* const* a_src, const uint32_t* b_q, const uint16_t* b_s,
+                                           int b_lds_row, int nsteps, int wm, int wn, int ni,
+                                           _Float16 (*As)[kLdsStride], _Float16 (*Bs)[kLdsStride],
+                                           float4_t (&acc)[4][8]) {
+    const int lane = threadIdx.x & 63;
+    GemmStage st;
+    gemm_load(st, a_src, b_q, b_s, 0);
+    for (int ks = 0; ks < nsteps; ++ks) {
+        gemm_store(st, As, Bs, b_lds_row);
+        __syncthreads();
+        gemm_load(st, a_src, b_q, b_s, min(ks + 1, nsteps - 1));   // the last reload is unused
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int kofs = kk * 32 + 8 * (lane >> 4);
+            half8_t a[4], b[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = lds_frag(&As[64 * wm + 16 * i + (lane & 15)][kofs]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b[j] = lds_frag(&Bs[128 * wn + 16 * j + (lane & 15)][kofs]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i >= ni) continue;                      // slice beyond the bucket
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// gate/up: B rows 0..127 are gate rows f0.., 128..255 the up rows f0..
 __global__ __launch_bounds__(256, 2) void gemm_gateup_kernel(moe_experts_t ex, const uint16_t* __restrict__ x16,
                                                              const int4* __restrict__ tiles,
                                                              const int* __restrict__ ntiles,
@@ -150,104 +222,53 @@ __global__ __launch_bounds__(256, 2) void gemm_gateup_kernel(moe_experts_t ex, c
     const int e = tile.x, r0 = tile.y, r1 = tile.z;
     const int f0 = nt * kGateUpBN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = __builtin_amdgcn_readfirstlane(wave & 1), wn = __builtin_amdgcn_readfirstlane(wave >> 1);
+    const int ni = __builtin_amdgcn_readfirstlane(min(4, max(0, (r1 - r0 - 64 * wm + 15) >> 4)));
 
     __shared__ _Float16 As[kGemmBM][kLdsStride];
     __shared__ _Float16 Bs[2 * kGateUpBN][kLdsStride];
 
-    // A gather: thread owns rows (tid >> 3) + 32 i, 16-byte column chunk tid & 7
-    const int a_col = (tid & 7) * 8;
     const uint16_t* a_src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        const int q = r0 + row;
+        const int q = r0 + (tid >> 3) + 32 * i;
         const int p = q < r1 ? pairs[q] : -1;
-        a_src[i] = (p >= 0 && p < P) ? x16 + (size_t)(p / K) * D + a_col : nullptr;
+        a_src[i] = (p >= 0 && p < P) ? x16 + (size_t)(p / K) * D + (tid & 7) * 8 : nullptr;
     }
-    // B: thread owns W row (tid >> 1) (gate rows then up rows), block tid & 1
-    const int b_row = tid >> 1, b_blk = tid & 1;
+    const int b_row = tid;
     const int wf = f0 + (b_row & (kGateUpBN - 1));
     const size_t b_rowidx = ((size_t)e * F + wf) * nkb;
     const uint32_t* b_q = (b_row < kGateUpBN ? ex.gate_q : ex.up_q) + b_rowidx * 2;
     const uint16_t* b_s = (b_row < kGateUpBN ? ex.gate_s : ex.up_s) + b_rowidx;
+    // wave wn needs gate rows 64 wn .. and up rows 128 + 64 wn ..: they are
+    // made contiguous (LDS rows 128 wn .. +128) by permuting the row order;
+    // tiles j < 4 are gate columns, j >= 4 the same up columns
+    const int b_lds_row = 128 * ((b_row & 127) >> 6) + (b_row >= kGateUpBN ? 64 : 0) + (b_row & 63);
 
-    float4_t acc_g[4][2], acc_u[4][2];
+    float4_t acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            acc_g[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-            acc_u[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < 8; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    gemm_kloop(a_src, b_q, b_s, b_lds_row, D / kGemmBK, wm, wn, ni, As, Bs, acc);
 
-    uint4 a_reg[4];
-    uint2 b_reg;
-    uint16_t s_reg;
-    auto load_stage = [&](int ks) {
-        const int k0 = ks * kGemmBK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a_reg[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-        const int kb = ks * 2 + b_blk;
-        b_reg = *reinterpret_cast<const uint2*>(b_q + (size_t)kb * 2);
-        s_reg = b_s[kb];
-    };
-    const int nsteps = D / kGemmBK;
-    load_stage(0);
-    for (int ks = 0; ks < nsteps; ++ks) {
-        // registers -> LDS
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&As[(tid >> 3) + 32 * i][a_col]) = a_reg[i];
-        {
-            uint32_t o[16];
-            dequant_block2(b_reg.x, b_reg.y, s_reg, o);
-            uint4* dst = reinterpret_cast<uint4*>(&Bs[b_row][b_blk * 32]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        }
-        __syncthreads();
-        if (ks + 1 < nsteps) load_stage(ks + 1);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int kofs = kk * 32 + 8 * (lane >> 4);
-            half8_t a[4], bg[2], bu[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = lds_frag(&As[64 * wm + 16 * i + (lane & 15)][kofs]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                bg[j] = lds_frag(&Bs[32 * wn + 16 * j + (lane & 15)][kofs]);
-                bu[j] = lds_frag(&Bs[kGateUpBN + 32 * wn + 16 * j + (lane & 15)][kofs]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc_g[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bg[j], acc_g[i][j], 0, 0, 0);
-                    acc_u[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bu[j], acc_u[i][j], 0, 0, 0);
-                }
-        }
-        __syncthreads();
-    }
     // epilogue: h = silu(g) * u -> fp16, stored in bucket-row order, each
     // 32-block of d_ff in unpack pair order
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int f = f0 + 32 * wn + 16 * j + (lane & 15);
+        for (int j = 0; j < 4; ++j) {
+            const int f = f0 + 64 * wn + 16 * j + (lane & 15);
             const int fpos = (f & ~31) + perm32(f & 31);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int q = r0 + 64 * wm + 16 * i + 4 * (lane >> 4) + v;
-                if (q < r1) hbuf[(size_t)q * F + fpos] = f32_to_f16_bits(silu_mul(acc_g[i][j][v], acc_u[i][j][v]));
+                if (q < r1) hbuf[(size_t)q * F + fpos] = f32_to_f16_bits(silu_mul(acc[i][j][v], acc[i][4 + j][v]));
             }
         }
 }
 
-// --------------------------------------------------------- 4. down GEMM
-// wave tile = 64 rows x 64 columns
+// down: B rows are d_model rows n0 ..
 __global__ __launch_bounds__(256, 2) void gemm_down_kernel(moe_experts_t ex, const uint16_t* __restrict__ hbuf,
                                                            const int4* __restrict__ tiles,
                                                            const int* __restrict__ ntiles,
@@ -264,72 +285,30 @@ __global__ __launch_bounds__(256, 2) void gemm_down_kernel(moe_experts_t ex, con
     const int e = tile.x, r0 = tile.y, r1 = tile.z;
     const int n0 = nt * kDownBN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = __builtin_amdgcn_readfirstlane(wave & 1), wn = __builtin_amdgcn_readfirstlane(wave >> 1);
+    const int ni = __builtin_amdgcn_readfirstlane(min(4, max(0, (r1 - r0 - 64 * wm + 15) >> 4)));
 
     __shared__ _Float16 As[kGemmBM][kLdsStride];
     __shared__ _Float16 Bs[kDownBN][kLdsStride];
 
-    const int a_col = (tid & 7) * 8;
     const uint16_t* a_src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = r0 + (tid >> 3) + 32 * i;
-        a_src[i] = q < r1 ? hbuf + (size_t)q * F + a_col : nullptr;
+        a_src[i] = q < r1 ? hbuf + (size_t)q * F + (tid & 7) * 8 : nullptr;
     }
-    const int b_row = tid >> 1, b_blk = tid & 1;
+    const int b_row = tid;
     const size_t b_rowidx = ((size_t)e * D + n0 + b_row) * nkb;
     const uint32_t* b_q = ex.down_q + b_rowidx * 2;
     const uint16_t* b_s = ex.down_s + b_rowidx;
 
-    float4_t acc[4][4];
+    float4_t acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    gemm_kloop(a_src, b_q, b_s, b_row, F / kGemmBK, wm, wn, ni, As, Bs, acc);
 
-    uint4 a_reg[4];
-    uint2 b_reg;
-    uint16_t s_reg;
-    auto load_stage = [&](int ks) {
-        const int k0 = ks * kGemmBK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a_reg[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-        const int kb = ks * 2 + b_blk;
-        b_reg = *reinterpret_cast<const uint2*>(b_q + (size_t)kb * 2);
-        s_reg = b_s[kb];
-    };
-    const int nsteps = F / kGemmBK;
-    load_stage(0);
-    for (int ks = 0; ks < nsteps; ++ks) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&As[(tid >> 3) + 32 * i][a_col]) = a_reg[i];
-        {
-            uint32_t o[16];
-            dequant_block2(b_reg.x, b_reg.y, s_reg, o);
-            uint4* dst = reinterpret_cast<uint4*>(&Bs[b_row][b_blk * 32]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        }
-        __syncthreads();
-        if (ks + 1 < nsteps) load_stage(ks + 1);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int kofs = kk * 32 + 8 * (lane >> 4);
-            half8_t a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = lds_frag(&As[64 * wm + 16 * i + (lane & 15)][kofs]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = lds_frag(&Bs[64 * wn + 16 * j + (lane & 15)][kofs]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        __syncthreads();
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -340,8 +319,8 @@ __global__ __launch_bounds__(256, 2) void gemm_down_kernel(moe_experts_t ex, con
             if (p < 0 || p >= P) continue;
             const float g = gates[p];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = n0 + 64 * wn + 16 * j + (lane & 15);
+            for (int j = 0; j < 8; ++j) {
+                const int n = n0 + 128 * wn + 16 * j + (lane & 15);
                 obuf[(size_t)p * D + n] = g * acc[i][j][v];
             }
         }
