@@ -311,14 +311,28 @@ __device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, LdsCo
     return *s_flag != 0;
 }
 
+// Levels of a block as 16 fp16 pairs in unpack order: pair m < 8 holds
+// weights (m, m + 8), pair 8 + m weights (16 + m, 24 + m).
+// 2-bit: the code of weight m sits at bits 2m of the word's low half and the
+// code of weight m + 8 at bits 2m of its high half.  OR-ing the masked word
+// into the mantissa of 1024.0 gives 1024 + code * 4^m' (m' = m, or m - 5
+// after one shift by 10 so the bits stay inside the 10-bit mantissa); one
+// fused multiply-add by 4^-m' and -(1024 * 4^-m' + 2) yields code - 2,
+// exactly, in both halves.
 template <int BITS>
 __device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
     if constexpr (BITS == 2) {
-        const half2_t bias = {(_Float16)-1026.0f, (_Float16)-1026.0f};
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            lv[m] = as_u32(as_half2(codes2_pair(w[0], 2 * m)) + bias);
-            lv[8 + m] = as_u32(as_half2(codes2_pair(w[1], 2 * m)) + bias);
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t w0 = w[h], w10 = w[h] >> 10;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int mm = m < 5 ? m : m - 5;
+                const uint32_t v = ((m < 5 ? w0 : w10) & (0x00030003u << (2 * mm))) | 0x64006400u;
+                const _Float16 mul = (_Float16)(1.0f / (float)(1 << (2 * mm)));
+                const _Float16 add = (_Float16)(-(1024.0f / (float)(1 << (2 * mm)) + 2.0f));
+                lv[8 * h + m] = as_u32(__builtin_elementwise_fma(as_half2(v), half2_t{mul, mul}, half2_t{add, add}));
+            }
         }
     } else {
         const half2_t bias = {(_Float16)-1028.0f, (_Float16)-1028.0f};
@@ -383,12 +397,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     const int d_lo = min(w * DPW, D), d_hi = min(d_lo + DPW, D);
     const int nrows = d_hi - d_lo;
 
-    float* us = reinterpret_cast<float*>(lds + P.lds_us);                 // [T][D]
     _Float16* xh = reinterpret_cast<_Float16*>(lds + P.lds_xh);           // [T][D/32][17 words]
     const uint32_t* xhw = reinterpret_cast<const uint32_t*>(lds + P.lds_xh);
     float* part = reinterpret_cast<float*>(lds + P.lds_part);             // [PT][DPW][nkbF]
     double* s_z = reinterpret_cast<double*>(lds + P.lds_part);            // [T][E] (dead before part is used)
-    float* s_z_f = reinterpret_cast<float*>(lds + P.lds_us);              // [PT][DPW] in DOWN (us is dead there)
+    float* s_z_f = reinterpret_cast<float*>(lds + P.lds_us);              // [PT][DPW] per-pair sums in DOWN
     uint32_t* pre = reinterpret_cast<uint32_t*>(lds + P.lds_pre);         // prefetched down blocks
     unsigned char* misc = lds + P.lds_misc;
     int* s_ids = reinterpret_cast<int*>(misc);                            // [PT]
@@ -399,8 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     double* s_red = reinterpret_cast<double*>(misc + misc_head_bytes(PT, T));   // [4][kMaxEPW][T]
     float* s_hloc = reinterpret_cast<float*>(s_red + 4 * kMaxEPW * T);    // see hloc_floats
     int* s_misc = reinterpret_cast<int*>(s_hloc + hloc_floats(DPW, T));   // [0] = U, [1] = flag
-    double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [T]
-    float* s_hres = reinterpret_cast<float*>(s_r + T);                    // [T][DPW] own residual rows
+    double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [4][T] per-wave sums of squares
+    float* s_hres = reinterpret_cast<float*>(s_r + 4 * T);                // [T][DPW] own residual rows
 
     const size_t zb_layer = (size_t)G * T * kZW;
     const size_t hb_layer = (size_t)G * T * kHW;
@@ -435,84 +448,82 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             const int j = tid / T, e = w * EPW + j;
             if (j < EPW && e < E) bias_v = m.router_b[(size_t)l * E + e];
         }
-        if (l == 0) {
-            for (int i = tid; i < T * D; i += kThreads)
-            {
-                const float v = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[i]) : ((const float*)P.x)[i];
-                us[i] = v;
-                xh[xh_half_index(i / D, nkbD, i % D)] = (_Float16)v;
-            }
-        } else {
-            const double* sbp = P.sb + (size_t)(l - 1) * sb_layer;
-            const float* hbp = P.hb + (size_t)(l - 1) * hb_layer;
-            const int q4 = (DPW + 3) >> 2;            // float4 per slice
-            const int nq = G * T * q4;
-            // issue every load of the phase first
-            float4 hv4[4];
+        {
+            // Thread tid owns elements d = tid + 256 k of every token: it loads
+            // them (x, or the residual slices the workgroups published), forms
+            // u, stores u's fp16 pairs for the expert phase and accumulates its
+            // share of this workgroup's logits, with no barrier in between.
+            const float* hbp = P.hb + (size_t)(l > 0 ? l - 1 : 0) * hb_layer;
+            constexpr int KR = T >= 16 ? 1 : 16 / T;      // elements per token per round of loads
+            float hv[KR][T];
+            auto load_round = [&](int k0) {
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int i = tid + kThreads * n;
-                if (i < nq) {
-                    const int g = i / (T * q4), rem = i - g * T * q4, t = rem / q4, c = rem - t * q4;
-                    hv4[n] = *reinterpret_cast<const float4*>(hbp + ((size_t)g * T + t) * kHW + 4 * c);
-                }
-            }
-            double ssv[T];
+                for (int kr = 0; kr < KR; ++kr) {
+                    const int d = min(tid + (k0 + kr) * kThreads, D - 1);
 #pragma unroll
-            for (int t = 0; t < T; ++t) ssv[t] = tid < G ? sbp[(size_t)tid * 16 + t] : 0.0;
-            for (int g = tid + kThreads; g < G; g += kThreads)
-#pragma unroll
-                for (int t = 0; t < T; ++t) ssv[t] += sbp[(size_t)g * 16 + t];
-            // sums of squares: fixed order (threads over workgroups, DPP, waves in order)
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const double v = wave_sum_f64(ssv[t]);
-                if (lane == 0) s_red[wave * T + t] = v;
-            }
-            __syncthreads();
-            if (tid < T) {
-                const double ss = ((s_red[tid] + s_red[T + tid]) + s_red[2 * T + tid]) + s_red[3 * T + tid];
-                s_r[tid] = sqrt(ss / (double)D + P.eps);
-            }
-            __syncthreads();
-            auto put = [&](int i, const float4& v) {
-                const int g = i / (T * q4), rem = i - g * T * q4, t = rem / q4, c = rem - t * q4;
-                const float vv[4] = {v.x, v.y, v.z, v.w};
-                const double r = s_r[t];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int d = g * DPW + 4 * c + k;
-                    if (4 * c + k < DPW && d < D) {
-                        const float uv = (float)((double)vv[k] / r);
-                        us[t * D + d] = uv;
-                        xh[xh_half_index(t, nkbD, d)] = (_Float16)uv;
+                    for (int t = 0; t < T; ++t) {
+                        if (l == 0) {
+                            const size_t xi = (size_t)t * D + d;
+                            hv[kr][t] = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[xi]) : ((const float*)P.x)[xi];
+                        } else {
+                            const int g = d / DPW;
+                            hv[kr][t] = hbp[((size_t)g * T + t) * kHW + (d - g * DPW)];
+                        }
                     }
                 }
             };
+            load_round(0);                                // in flight during the sums of squares
+            double rr[T], inv[T];
+            if (l > 0) {
+                // sums of squares: thread g loads workgroup g's sum (threads
+                // over workgroups, then DPP, then the 4 waves in order); every
+                // thread then forms the same rms from the 4 wave sums
+                const double* sbp = P.sb + (size_t)(l - 1) * sb_layer;
+                double ss[T];
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int i = tid + kThreads * n;
-                if (i < nq) put(i, hv4[n]);
+                for (int t = 0; t < T; ++t) ss[t] = tid < G ? sbp[(size_t)tid * 16 + t] : 0.0;
+                for (int g = tid + kThreads; g < G; g += kThreads)
+#pragma unroll
+                    for (int t = 0; t < T; ++t) ss[t] += sbp[(size_t)g * 16 + t];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const double v = wave_sum_f64(ss[t]);
+                    if (lane == 0) s_r[wave * T + t] = v;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const double tot = ((s_r[t] + s_r[T + t]) + s_r[2 * T + t]) + s_r[3 * T + t];
+                    rr[t] = sqrt(tot / (double)D + P.eps);
+                    inv[t] = 1.0 / rr[t];
+                }
             }
-            for (int i = tid + 4 * kThreads; i < nq; i += kThreads) {
-                const int g = i / (T * q4), rem = i - g * T * q4, t = rem / q4, c = rem - t * q4;
-                put(i, *reinterpret_cast<const float4*>(hbp + ((size_t)g * T + t) * kHW + 4 * c));
-            }
-        }
-        __syncthreads();
-        {
             double acc[kMaxEPW][T];
 #pragma unroll
             for (int j = 0; j < kMaxEPW; ++j)
 #pragma unroll
                 for (int t = 0; t < T; ++t) acc[j][t] = 0.0;
-            for (int d = tid; d < D; d += kThreads) {
+            for (int k0 = 0; k0 * kThreads < D; k0 += KR) {
+                if (k0 > 0) load_round(k0);
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const double uv = (double)us[t * D + d];
+                for (int kr = 0; kr < KR; ++kr) {
+                    const int d = tid + (k0 + kr) * kThreads;
+                    if (d >= D) continue;
 #pragma unroll
-                    for (int j = 0; j < kMaxEPW; ++j)
-                        if (j < my_experts) acc[j][t] = fma(uv, (double)wr_lds[j * D + d], acc[j][t]);
+                    for (int t = 0; t < T; ++t) {
+                        float uv = hv[kr][t];
+                        if (l > 0) {
+                            // h / r correctly rounded: reciprocal, then one
+                            // remainder correction (Markstein)
+                            const double hd = (double)uv;
+                            const double q0 = hd * inv[t];
+                            uv = (float)fma(fma(-q0, rr[t], hd), inv[t], q0);
+                        }
+                        xh[xh_half_index(t, nkbD, d)] = (_Float16)uv;
+#pragma unroll
+                        for (int j = 0; j < kMaxEPW; ++j)
+                            if (j < my_experts) acc[j][t] = fma((double)uv, (double)wr_lds[j * D + d], acc[j][t]);
+                    }
                 }
             }
 #pragma unroll
@@ -583,25 +594,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         // distinct experts of the batch, in slot order of first appearance
         if (PT <= 64) {
             if (wave == 0) {
+                // lane p holds pair p; its expert's first pair is the lowest q
+                // with the same id; first pairs are numbered by a ballot
                 const int e = lane < PT ? s_ids[lane] : -1;
-                int first = lane < PT;
-                for (int q = 0; q < PT; ++q) {
-                    const int eq = __builtin_amdgcn_readlane(e, q);
-                    first &= !(q < lane && eq == e);
-                }
+                int firstq = lane;
+                for (int q = PT - 1; q >= 0; --q)
+                    if (__builtin_amdgcn_readlane(e, q) == e) firstq = q;
+                const bool first = lane < PT && firstq == lane;
                 const unsigned long long fm = __ballot(first);
-                if (first) {
-                    const int idx = __popcll(fm & ((1ull << lane) - 1ull));
-                    s_uniq[idx] = e;
-                    int pr[T];
-#pragma unroll
-                    for (int t = 0; t < T; ++t) pr[t] = -1;
-                    for (int q = 0; q < PT; ++q)
-                        if (__builtin_amdgcn_readlane(e, q) == e) pr[q / K] = q;
-#pragma unroll
-                    for (int t = 0; t < T; ++t) s_upair[idx * T + t] = (short)pr[t];
-                }
-                if (lane == 0) s_misc[0] = __popcll(fm);
+                const int idx = __popcll(fm & ((1ull << lane) - 1ull));
+                const int U = __popcll(fm);
+                if (first) s_uniq[idx] = e;
+                for (int i = lane; i < U * T; i += 64) s_upair[i] = (short)-1;
+                const int my_u = __shfl(idx, firstq);             // distinct-expert number of pair p
+                if (lane < PT) s_upair[my_u * T + lane / K] = (short)lane;
+                if (lane == 0) s_misc[0] = U;
             }
         } else {
             for (int p = tid; p < PT; p += kThreads) {
@@ -949,9 +956,8 @@ static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bit
     const int W = bits == 2 ? 2 : 3;
     const int nkbF = F / 32;
     size_t off = 0;
-    p.us = off;                        // u rows; in DOWN the per-pair sums [PT][DPW]
-    const size_t us_floats = (size_t)T * D > (size_t)PT * DPW ? (size_t)T * D : (size_t)PT * DPW;
-    off += align256(sizeof(float) * us_floats);
+    p.us = off;                        // per-pair sums [PT][DPW] of the DOWN phase
+    off += align256(sizeof(float) * (size_t)PT * DPW);
     // ROUTE and FFN: logits [T][E] doubles, then u in fp16 pair order
     // (padded); DOWN: per-block partial sums [PT][DPW][F/32] floats
     p.part = off;
@@ -964,7 +970,7 @@ static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bit
     off += align256(sizeof(float) * (size_t)EPW * D);
     p.misc = off;
     size_t mb = (size_t)misc_head_bytes(PT, T);
-    mb += sizeof(double) * 4 * kMaxEPW * T + sizeof(float) * hloc_floats(DPW, T) + 16 + sizeof(double) * T +
+    mb += sizeof(double) * 4 * kMaxEPW * T + sizeof(float) * hloc_floats(DPW, T) + 16 + sizeof(double) * 4 * T +
           sizeof(float) * (size_t)T * DPW;
     off += align256(mb);
     p.pre = off;
