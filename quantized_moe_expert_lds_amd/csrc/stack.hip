@@ -168,9 +168,10 @@ __device__ __forceinline__ double wave_max_f64(double v) {
     return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
                             __builtin_amdgcn_readlane(__double2loint(v), 63));
 }
+// identity "old" values with bound_ctrl let each step fold into one DPP op
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ int dpp_mini(int v) {
-    return min(v, __builtin_amdgcn_update_dpp(v, v, CTRL, ROWMASK, 0xf, false));
+    return min(v, __builtin_amdgcn_update_dpp(0x7fffffff, v, CTRL, ROWMASK, 0xf, true));
 }
 __device__ __forceinline__ int wave_min_i32(int v) {
     v = dpp_mini<0x111, 0xf>(v);
@@ -184,7 +185,7 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ unsigned dpp_maxu(unsigned v) {
-    return max(v, (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWMASK, 0xf, false));
+    return max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xf, true));
 }
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
     v = dpp_maxu<0x111, 0xf>(v);
@@ -208,23 +209,25 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
                             __builtin_amdgcn_readlane(__double2loint(v), l));
 }
 
-// Top-k of z[0..E) (E <= 64 * kPer) by one wavefront, ranked by (z desc, id
-// asc), with softmax gates over the k selected logits.  Each lane sorts its
-// kPer values (ids ascending; a stable sort on value keeps equal values in id
-// order), so a lane's head is its best element.  Each round finds the best
-// head: the largest 32-bit order key over the heads (one DPP max per step)
-// decides alone when a single lane holds it; otherwise the fp64 values and
-// then the ids of the tied lanes decide.  The winning lane pops its head.
+// Top-k of z[e_lo..e_hi) (at most 64 * kPer values) by one wavefront,
+// ranked by (z desc, id asc), written in rank order to out_v / out_i (and
+// the 32-bit order keys to out_k).  Each lane sorts its kPer values (ids
+// ascending; a stable sort on value keeps equal values in id order), so a
+// lane's head is its best element.  Each round takes the largest 32-bit
+// order key over the heads (one DPP max per step); when a single lane holds
+// it, that lane writes its head and pops it.  A tie on the key bits is
+// settled by the fp64 values and then the ids of the tied lanes.
 template <int kPer>
-__device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* gates) {
+__device__ void wave_topk_core(const double* z, int e_lo, int e_hi, int K, double* out_v, int* out_i,
+                               unsigned* out_k) {
     const int lane = threadIdx.x & 63;
     double v[kPer];
     int id[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? z[e] + 0.0 : -INFINITY;
-        id[i] = e < E ? e : 0x7fffffff;
+        const int e = e_lo + lane + 64 * i;
+        v[i] = e < e_hi ? z[e] + 0.0 : -INFINITY;
+        id[i] = e < e_hi ? e : 0x7fffffff;
     }
 #pragma unroll
     for (int a = 1; a < kPer; ++a)
@@ -238,21 +241,20 @@ __device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* ga
             v[b - 1] = sw ? tv : v[b - 1];
             id[b - 1] = sw ? ti : id[b - 1];
         }
-    double mine = 0.0;
     for (int j = 0; j < K; ++j) {
         const unsigned key = order_hi(v[0]);
         const unsigned mk = wave_max_u32(key);
-        unsigned long long cand = __ballot(key == mk);
-        if (__popcll(cand) > 1) {
+        bool win = key == mk;
+        if (__popcll(__ballot(win)) > 1) {
             // tie on the high key bits: exact value, then lowest id
-            const double M = wave_max_f64(key == mk ? v[0] : -INFINITY);
-            const int wid = wave_min_i32(key == mk && v[0] == M ? id[0] : 0x7fffffff);
-            cand = __ballot(key == mk && id[0] == wid);
+            const double M = wave_max_f64(win ? v[0] : -INFINITY);
+            const int wid = wave_min_i32(win && v[0] == M ? id[0] : 0x7fffffff);
+            win = win && id[0] == wid;
         }
-        const int wl = __ffsll((long long)cand) - 1;
-        const double M = readlane_f64(v[0], wl);
-        const int win = __builtin_amdgcn_readlane(id[0], wl);
-        if (lane == wl) {
+        if (win) {
+            out_v[j] = v[0];
+            out_i[j] = id[0];
+            out_k[j] = key;
 #pragma unroll
             for (int i = 0; i < kPer - 1; ++i) {
                 v[i] = v[i + 1];
@@ -261,15 +263,51 @@ __device__ void wave_topk_dpp(const double* z, int E, int K, int* ids, float* ga
             v[kPer - 1] = -INFINITY;
             id[kPer - 1] = 0x7fffffff;
         }
-        if (lane == j) {
-            mine = M;
-            ids[j] = win;
-        }
     }
-    const double m0 = readlane_f64(mine, 0);
+}
+
+// softmax gates over K sorted logits (LDS, rank order)
+__device__ __forceinline__ void wave_gates(const double* sv, const int* si, int K, int* ids, float* gates) {
+    const int lane = threadIdx.x & 63;
+    const double mine = lane < K ? sv[lane] : 0.0;
+    const double m0 = sv[0];
     const double p = lane < K ? exp(mine - m0) : 0.0;
     const double sum = wave_sum_f64(p);
-    if (lane < K) gates[lane] = (float)(p / sum);
+    if (lane < K) {
+        ids[lane] = si[lane];
+        gates[lane] = (float)(p / sum);
+    }
+}
+
+// Merge C <= 64 candidates (value, id, key; C a multiple of 4) into the top
+// K by rank counting: a candidate's rank is the number of candidates ranked
+// before it; distinct 32-bit order keys decide alone, ties on them use the
+// exact values and ids.  Writes rank order to out_v / out_i.
+__device__ void wave_merge_topk(const double* cv, const int* ci, const unsigned* ck, int C, int K, double* out_v,
+                                int* out_i) {
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < C;
+    const double v = valid ? cv[lane] : -INFINITY;
+    const int id = valid ? ci[lane] : 0x7fffffff;
+    const unsigned key = valid ? ck[lane] : 0u;
+    int rank = 0, eq = 0;
+    for (int q = 0; q < C; q += 4) {
+        const uint4 kq = *reinterpret_cast<const uint4*>(ck + q);          // same address in every lane
+        rank += (kq.x > key) + (kq.y > key) + (kq.z > key) + (kq.w > key);
+        eq += (kq.x == key) + (kq.y == key) + (kq.z == key) + (kq.w == key);
+    }
+    if (__ballot(valid && eq > 1)) {
+        rank = 0;
+        for (int q = 0; q < C; ++q) {
+            const double vq = cv[q];
+            const int iq = ci[q];
+            rank += (vq > v) || (vq == v && iq < id);
+        }
+    }
+    if (valid && rank < K) {
+        out_v[rank] = v;
+        out_i[rank] = id;
+    }
 }
 
 // Grid barrier number `epoch` (1-based).  Returns false if it timed out or
@@ -381,6 +419,13 @@ __host__ __device__ inline int hloc_floats(int DPW, int T) {
     const int b = 16 * T * kMaxItemsInFlight;
     return a > b ? a : b;
 }
+// byte offset (from the misc base) of the top-k candidate arrays, past
+// s_ids .. s_hres, 16-byte aligned
+__host__ __device__ inline int misc_tail_offset(int PT, int T, int DPW) {
+    const int end = misc_head_bytes(PT, T) + 8 * 4 * kMaxEPW * T + 4 * hloc_floats(DPW, T) + 16 + 8 * 4 * T +
+                    4 * T * DPW;
+    return (end + 15) & ~15;
+}
 
 template <int T, int BITS, int KPER>
 __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P) {
@@ -414,6 +459,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     int* s_misc = reinterpret_cast<int*>(s_hloc + hloc_floats(DPW, T));   // [0] = U, [1] = flag
     double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [4][T] per-wave sums of squares
     float* s_hres = reinterpret_cast<float*>(s_r + 4 * T);                // [T][DPW] own residual rows
+    double* s_cand_v = reinterpret_cast<double*>(misc + misc_tail_offset(PT, T, DPW));   // [256] top-k lists
+    int* s_cand_i = reinterpret_cast<int*>(s_cand_v + 256);               // [256]
+    unsigned* s_cand_k = reinterpret_cast<unsigned*>(s_cand_i + 256);     // [256]
 
     const size_t zb_layer = (size_t)G * T * kZW;
     const size_t hb_layer = (size_t)G * T * kHW;
@@ -583,7 +631,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
         }
         __syncthreads();
-        for (int t = wave; t < T; t += 4) wave_topk_dpp<KPER>(s_z + (size_t)t * E, E, K, s_ids + t * K, s_gates + t * K);
+        if (T == 1 && KPER >= 4 && 4 * K <= 64) {
+            // batch 1: each wave selects the top K of a quarter of the
+            // experts, then wave 0 merges the 4 K candidates
+            constexpr int kq = KPER >= 4 ? KPER / 4 : 1;
+            wave_topk_core<kq>(s_z, 64 * kq * wave, min(E, 64 * kq * (wave + 1)), K, s_cand_v + wave * K,
+                               s_cand_i + wave * K, s_cand_k + wave * K);
+            __syncthreads();
+            if (wave == 0) {
+                wave_merge_topk(s_cand_v, s_cand_i, s_cand_k, 4 * K, K, s_cand_v + 64, s_cand_i + 64);
+                wave_gates(s_cand_v + 64, s_cand_i + 64, K, s_ids, s_gates);
+            }
+        } else {
+            for (int t = wave; t < T; t += 4) {
+                double* ov = s_cand_v + 64 * wave;
+                int* oi = s_cand_i + 64 * wave;
+                wave_topk_core<KPER>(s_z + (size_t)t * E, 0, E, K, ov, oi, s_cand_k + 64 * wave);
+                wave_gates(ov, oi, K, s_ids + t * K, s_gates + t * K);
+            }
+        }
         __syncthreads();
         if (w == 0 && P.ids_out) {
             for (int i = tid; i < PT; i += kThreads) {
@@ -970,8 +1036,7 @@ static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bit
     off += align256(sizeof(float) * (size_t)EPW * D);
     p.misc = off;
     size_t mb = (size_t)misc_head_bytes(PT, T);
-    mb += sizeof(double) * 4 * kMaxEPW * T + sizeof(float) * hloc_floats(DPW, T) + 16 + sizeof(double) * 4 * T +
-          sizeof(float) * (size_t)T * DPW;
+    mb = (size_t)misc_tail_offset(PT, T, DPW) + 256 * (sizeof(double) + 2 * sizeof(int));
     off += align256(mb);
     p.pre = off;
     p.total = off;
