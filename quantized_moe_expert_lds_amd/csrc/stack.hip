@@ -349,6 +349,17 @@ __device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, LdsCo
     return *s_flag != 0;
 }
 
+// NB bits of the 96-bit string w[0] | w[1] << 32 | w[2] << 64 from bit p
+// (compile-time p after unrolling); bits past 96 read as zero
+template <int NB>
+__device__ __forceinline__ uint32_t bits96(const uint32_t* w, int p) {
+    const int k = p >> 5, off = p & 31;
+    const uint32_t lo = w[k];
+    const uint32_t hi = k + 1 < 3 ? w[k + 1] : 0u;
+    const uint32_t x = off + NB <= 32 ? (lo >> off) : __builtin_amdgcn_alignbit(hi, lo, off);
+    return x & ((1u << NB) - 1u);
+}
+
 // Levels of a block as 16 fp16 pairs in unpack order: pair m < 8 holds
 // weights (m, m + 8), pair 8 + m weights (16 + m, 24 + m).
 // 2-bit: the code of weight m sits at bits 2m of the word's low half and the
@@ -373,12 +384,29 @@ __device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
             }
         }
     } else {
-        const half2_t bias = {(_Float16)-1028.0f, (_Float16)-1028.0f};
+        // 3-bit: weight i sits at bits 3i of the 96-bit string w0 | w1 << 32
+        // | w2 << 64.  Pairs (m, m + 8) are built three at a time: the 9 bits
+        // of weights m0 .. m0+2 go to the low half of X and those of weights
+        // m0+8 .. m0+10 to the high half; pair j then is an and-or of the
+        // codes at bits 3j into the mantissa of 1024.0 (1024 + code * 8^j)
+        // and one fused multiply-add by 8^-j and -(1024 * 8^-j + 4).
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            lv[m] = as_u32(as_half2(codes3_pair(w[0], w[1], w[2], m)) + bias);
-            lv[8 + m] = as_u32(as_half2(codes3_pair(w[0], w[1], w[2], 16 + m)) + bias);
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const int m0 = 3 * g, nj = g < 2 ? 3 : 2;
+                const uint32_t lo = bits96<9>(w, 48 * h + 3 * m0);
+                const uint32_t hi = bits96<9>(w, 48 * h + 3 * m0 + 24);
+                const uint32_t X = lo | (hi << 16);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    if (j >= nj) continue;
+                    const uint32_t v = (X & (0x00070007u << (3 * j))) | 0x64006400u;
+                    const _Float16 mul = (_Float16)(1.0f / (float)(1 << (3 * j)));
+                    const _Float16 add = (_Float16)(-(1024.0f / (float)(1 << (3 * j)) + 4.0f));
+                    lv[8 * h + m0 + j] = as_u32(__builtin_elementwise_fma(as_half2(v), half2_t{mul, mul}, half2_t{add, add}));
+                }
+            }
     }
 }
 
