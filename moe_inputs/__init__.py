@@ -69,7 +69,7 @@ M2 = 0x94D049BB133111EB
 # tensor ids used in key derivation
 GATE, UP, DOWN, ROUTER, BIAS_PERM, ACT = 0, 1, 2, 3, 4, 5
 # model families: the tiny shapes and the full 2048/768/512 shapes
-FAMILY_TINY, FAMILY_FULL = 1, 2
+FAMILY_TINY, FAMILY_FULL, FAMILY_CODER = 1, 2, 3
 
 
 def mix64(z: int) -> int:
@@ -217,6 +217,10 @@ WORKLOADS = {
                  note="one 8,192-token prefill chunk through one layer"),
         Workload("verify4_3bit", FAMILY_FULL, 48, 512, 2048, 768, 10, 4, 3, "f32", True, True, act_tag=5,
                  note="4-token verify batch through 48 layers, 3-bit experts"),
+        # the pages' Coder build keeps about half of the experts; a short
+        # stack of such layers is a shape variant for the tests
+        Workload("coder_256", FAMILY_CODER, 4, 256, 2048, 768, 10, 2, 2, "f32", True, True, act_tag=6,
+                 note="4 layers x 256 experts, 2 tokens, 2-bit"),
     ]
 }
 

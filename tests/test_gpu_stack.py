@@ -3,6 +3,8 @@ launch) against the free-running CPU oracle, plus batch invariance,
 determinism across launches and the barrier error word."""
 from __future__ import annotations
 
+import copy
+import ctypes
 import sys
 
 import numpy as np
@@ -143,3 +145,103 @@ def test_stack_batch_of_8(q):
     assert torch.equal(h1[0], h[5])
     matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
     assert matched >= 1
+
+
+def test_stack_single_layer_bf16_matches_layer_calls(q):
+    _say("moe_decode_stack, single-layer decode (bf16 token, 512 experts) vs oracle and vs moe_route + moe_ffn_decode")
+    wl = mi.WORKLOADS["decode_1layer"]
+    st, ex, rw, rb = device_stack(wl)
+    x = mi.activations_host(wl)                       # bf16 bit patterns
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    h, ids, g, _ = run_stack(q, st, xd, 1)
+    # oracle: one layer, no norm before it: h = x + y
+    wh, bh = mi.router_host(wl, 0)
+    ids_o, gates_o, y_o = O.moe_layer(O.as_f32_activations(x), wh, bh, wl.top_k, oracle_experts(wl, 0, 2), 2)
+    assert np.array_equal(ids.cpu().numpy()[0], ids_o)
+    assert np.max(np.abs(g.cpu().numpy()[0] - gates_o)) <= TOL
+    want = (O.as_f32_activations(x) + y_o).astype(np.float32)
+    assert row_rel_err(h.cpu().numpy(), want) <= TOL
+    # the layer-by-layer calls agree on routing, and on the layer output to rounding
+    router = q.Router(rw[0], rb[0], wl.top_k)
+    experts = q.Experts(ex["gate_q"][0], ex["up_q"][0], ex["down_q"][0], ex["gate_s"][0], ex["up_s"][0],
+                        ex["down_s"][0], 2)
+    ids1 = torch.empty((1, wl.top_k), dtype=torch.int32, device="cuda")
+    w1 = torch.empty((1, wl.top_k), device="cuda")
+    q.moe_route(router, xd, ids1, w1, None, None, q.workspace(q.MOE_OP_ROUTE, 1, 2048, 768, 512, 10))
+    y1 = torch.empty((1, 2048), device="cuda")
+    q.moe_ffn_decode(experts, xd, ids1, w1, y1, q.workspace(q.MOE_OP_DECODE, 1, 2048, 768, 512, 10))
+    torch.cuda.synchronize()
+    assert torch.equal(ids1[0], ids[0, 0])
+    assert torch.max(torch.abs(w1[0] - g[0, 0])).item() <= 1e-6
+    h_layers = (xd.float() + y1).cpu().numpy()
+    assert row_rel_err(h.cpu().numpy(), h_layers) <= TOL
+    del st, ex, rw, rb
+    torch.cuda.empty_cache()
+
+
+def test_stack_256_experts_two_tokens(q):
+    _say("moe_decode_stack, 4 layers x 256 experts (one router expert per workgroup), T=2, batch invariance")
+    wl = mi.WORKLOADS["coder_256"]
+    st, ex, rw, rb = device_stack(wl)
+    x = mi.activations_host(wl)
+    xd = torch.from_numpy(x).cuda()
+    h, ids, g, _ = run_stack(q, st, xd, 2)
+    for t in range(2):
+        h1, ids1, g1, _ = run_stack(q, st, xd[t:t + 1].contiguous(), 1)
+        assert torch.equal(h1[0], h[t]) and torch.equal(ids1[:, 0], ids[:, t]) and torch.equal(g1[:, 0], g[:, t])
+    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
+    assert matched >= 1
+    del st, ex, rw, rb
+    torch.cuda.empty_cache()
+
+
+def test_stack_batch_of_3(q):
+    _say("moe_decode_stack, 4 layers, T=3 (odd batch) equals three batch-1 runs")
+    wl = mi.WORKLOADS["decode_48layer"]
+    st, ex, rw, rb = device_stack(wl, n_layers=4)
+    x = mi.activations_host(wl, 3, stream=7)
+    xd = torch.from_numpy(x).cuda()
+    h, ids, g, _ = run_stack(q, st, xd, 3)
+    for t in range(3):
+        h1, ids1, g1, _ = run_stack(q, st, xd[t:t + 1].contiguous(), 1)
+        assert torch.equal(h1[0], h[t]) and torch.equal(ids1[:, 0], ids[:, t]) and torch.equal(g1[:, 0], g[:, t])
+    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
+    assert matched >= 1
+    del st, ex, rw, rb
+    torch.cuda.empty_cache()
+
+
+def test_stack_abi_errors(q):
+    _say("moe_decode_stack argument checks (before any launch)")
+    wl = mi.WORKLOADS["tiny"]
+    st, ex, rw, rb = device_stack(wl)
+    x = torch.from_numpy(mi.activations_host(wl)).cuda()
+    h = torch.empty((8, 256), device="cuda")
+    ws = q.stack_workspace(st, 8)
+    lib = q.library
+
+    def call(stack, xx, n, hh, w, nbytes, ids=None, gates=None):
+        return lib.moe_decode_stack(ctypes.byref(stack._c), q._ptr(xx), q._dtype(xx), n, 1e-6, q._ptr(hh),
+                                    q._ptr(ids), q._ptr(gates), q._ptr(w), nbytes, None)
+
+    assert call(st, x, 8, h, ws, ws.numel()) == q.MOE_OK
+    torch.cuda.synchronize()
+    assert call(st, x, 0, h, ws, ws.numel()) == q.MOE_ERR_ARG
+    assert call(st, x, 9, h, ws, ws.numel()) == q.MOE_ERR_UNSUPPORTED          # more than 8 tokens
+    assert call(st, x, 8, h, None, 0) == q.MOE_ERR_WORKSPACE
+    assert call(st, x, 8, h, ws, 4096) == q.MOE_ERR_WORKSPACE                   # far below any grid's need
+    ids = torch.empty((1, 8, 2), dtype=torch.int32, device="cuda")
+    assert call(st, x, 8, h, ws, ws.numel(), ids=ids) == q.MOE_ERR_ARG           # ids without gates
+    bad = copy.copy(st)
+    bad._c = q._StackT.from_buffer_copy(st._c)
+    bad._c.bits = 4
+    assert call(bad, x, 8, h, ws, ws.numel()) == q.MOE_ERR_UNSUPPORTED
+    bad._c.bits = 2
+    bad._c.top_k = 17                                                           # k > experts
+    assert call(bad, x, 8, h, ws, ws.numel()) == q.MOE_ERR_UNSUPPORTED
+    bad._c.top_k = 2
+    bad._c.d_model = 250                                                        # not a multiple of 32
+    assert call(bad, x, 8, h, ws, ws.numel()) == q.MOE_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    err = int(ws[q.MOE_STACK_ERROR_OFFSET:q.MOE_STACK_ERROR_OFFSET + 4].view(torch.int32).item())
+    assert err == 0
