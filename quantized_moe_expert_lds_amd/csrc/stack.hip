@@ -949,16 +949,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             for (int o = tid; o < PT * nrows; o += kThreads) {
                 const int p = o / nrows, r = o - p * nrows;
                 const float* pp = part + ((size_t)p * DPW + r) * nkbF;
+                // blocks added in order; reads issued 8 at a time
                 float oj = 0.0f;
-                for (int kb = 0; kb < nkbF; ++kb) oj += pp[kb];
+                int kb = 0;
+                for (; kb + 8 <= nkbF; kb += 8) {
+                    float v[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[i] = pp[kb + i];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) oj += v[i];
+                }
+                for (; kb < nkbF; ++kb) oj += pp[kb];
                 s_o[p * DPW + r] = oj;
             }
             __syncthreads();
             // y rows (slots in order with their gates), residual, sums of squares
             for (int o = tid; o < T * nrows; o += kThreads) {
                 const int t = o / nrows, r = o - t * nrows;
+                // slots added in order with their gates; reads issued 8 at a time
                 float yv = 0.0f;
-                for (int j = 0; j < K; ++j) yv = yv + s_gates[t * K + j] * s_o[(t * K + j) * DPW + r];
+                int j = 0;
+                for (; j + 8 <= K; j += 8) {
+                    float gv[8], ov[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        gv[i] = s_gates[t * K + j + i];
+                        ov[i] = s_o[(t * K + j + i) * DPW + r];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) yv = yv + gv[i] * ov[i];
+                }
+                for (; j < K; ++j) yv = yv + s_gates[t * K + j] * s_o[(t * K + j) * DPW + r];
                 const int d = d_lo + r;
                 const float hn = s_hres[t * DPW + r] + yv;
                 s_hres[t * DPW + r] = hn;
