@@ -105,6 +105,10 @@ struct LdsCopy {
     int bytes;
 };
 
+struct NoSideWork {
+    __device__ void operator()() const {}
+};
+
 // ------------------------------------------------------- coherent stores
 __device__ __forceinline__ void st_f32(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -314,13 +318,15 @@ __device__ void wave_merge_topk(const double* cv, const int* ci, const unsigned*
 // another workgroup reported an error.
 // Waves 1..3 may start an LDS copy (`cp`) while wave 0 waits; it completes
 // by the next barrier.
-__device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, LdsCopy cp = {nullptr, nullptr, 0}) {
+// Waves 1-3 run `side` (copies into LDS) while wave 0 waits for the grid.
+template <typename Side = NoSideWork>
+__device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, Side side = Side{}) {
     // every thread waits until its own stores have completed (gfx9 counts
     // stores in vmcnt; a workgroup-scope release fence emits no wait)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int* sync = P.sync;
-    if (threadIdx.x >= 64 && cp.bytes > 0) dma_to_lds(cp.src, cp.dst, cp.bytes, 1, 3);
+    if (threadIdx.x >= 64) side();
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         if (lane == 0)
@@ -626,7 +632,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         // the next layer's router rows stream in while this barrier waits
         // (every wave is done reading wr_lds once the barrier's entry
         // __syncthreads has passed)
-        if (!grid_barrier(P, ++epoch, &s_misc[1], l + 1 < L && my_experts > 0 ? router_copy(l + 1) : LdsCopy{nullptr, nullptr, 0}))
+        if (!grid_barrier(P, ++epoch, &s_misc[1], [&]() {
+                if (l + 1 < L && my_experts > 0) {
+                    const LdsCopy c = router_copy(l + 1);
+                    dma_to_lds(c.src, c.dst, c.bytes, 1, 3);
+                }
+            }))
             return;
 
         // --------------------------------------------------------------- FFN
@@ -735,16 +746,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         const int U = s_misc[0];
 
         const size_t lstrideD = (size_t)E * D * nkbF;
-        // Copies into LDS make the compiler wait for them before any later
-        // LDS access, so everything this phase reads from LDS before its
-        // weight loads is read first, and the copies are issued right after
-        // those loads.
         const int uid = lane < U ? s_uniq[lane] : 0;     // distinct expert `lane` (first 64)
         const int n_pre = min(U, P.pre_cap);
         // copy this workgroup's down-projection rows d_lo .. d_hi of the first
-        // n_pre distinct experts into LDS (used after the next barrier);
-        // chunks are dealt to the waves round-robin.  Wave-uniform control
-        // flow only: every lane of the wave takes part in a chunk.
+        // n_pre distinct experts into LDS.  Waves 1-3 issue the copies while
+        // wave 0 waits at the next grid barrier, so they do not compete with
+        // the gate/up weight loads; chunks are dealt to the three waves
+        // round-robin.  Wave-uniform control flow only: every lane of the
+        // wave takes part in a chunk.
         auto issue_down_prefetch = [&]() {
             if (nrows <= 0) return;
             const int cbytes = nrows * nkbF * W * 4, sbytes = nrows * nkbF * 2;
@@ -756,12 +765,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 const char* ssrc = reinterpret_cast<const char*>(m.down_s + row0 * nkbF);
                 char* cdst = reinterpret_cast<char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
                 for (int off = 0; off < cbytes; off += 64 * P.pre_cgran, ++ci)
-                    if ((ci & 3) == wave) dma_chunk(csrc, cdst, off, cbytes, P.pre_cgran);
+                    if (ci % 3 == wave - 1) dma_chunk(csrc, cdst, off, cbytes, P.pre_cgran);
                 for (int off = 0; off < sbytes; off += 64 * P.pre_sgran, ++ci)
-                    if ((ci & 3) == wave) dma_chunk(ssrc, cdst + P.pre_cstride, off, sbytes, P.pre_sgran);
+                    if (ci % 3 == wave - 1) dma_chunk(ssrc, cdst + P.pre_cstride, off, sbytes, P.pre_sgran);
             }
         };
-        bool prefetch_pending = true;
 
         {
             const int n_items = U * nch;
@@ -812,10 +820,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                             load_block<W>(r < 4 ? m.gate_q : m.up_q, blk, q[a][r]);
                             sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
                         }
-                    }
-                    if (prefetch_pending) {
-                        prefetch_pending = false;
-                        issue_down_prefetch();
                     }
                     uint32_t xpk[T][16];
                     if (kb0 > 0) {
@@ -872,8 +876,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 __syncthreads();
             }
         }
-        if (prefetch_pending) issue_down_prefetch();      // workgroups without gate/up items
-        if (!grid_barrier(P, ++epoch, &s_misc[1])) return;
+        // the copies must have landed before any wave reads them after the barrier
+        if (!grid_barrier(P, ++epoch, &s_misc[1], [&]() {
+                issue_down_prefetch();
+                __builtin_amdgcn_s_waitcnt(0);
+            }))
+            return;
 
         // -------------------------------------------------------------- DOWN
         {
