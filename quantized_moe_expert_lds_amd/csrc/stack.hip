@@ -374,8 +374,30 @@ __device__ __forceinline__ uint32_t bits96(const uint32_t* w, int p) {
 // after one shift by 10 so the bits stay inside the 10-bit mantissa); one
 // fused multiply-add by 4^-m' and -(1024 * 4^-m' + 2) yields code - 2,
 // exactly, in both halves.
+//
+// The and-or is one v_and_or_b32 only when its two constants sit in
+// registers (a three-operand instruction takes no literal on gfx9), so the
+// constants are made once per kernel and hidden from constant folding.
+struct UnpackConsts {
+    uint32_t magic;      // 0x64006400 (1024.0 in both halves), in a VGPR
+    uint32_t mask[5];    // code masks, in SGPRs
+};
+
 template <int BITS>
-__device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
+__device__ __forceinline__ UnpackConsts make_unpack_consts() {
+    UnpackConsts k;
+    k.magic = 0x64006400u;
+    asm("" : "+v"(k.magic));
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        k.mask[j] = BITS == 2 ? 0x00030003u << (2 * j) : (j < 3 ? 0x00070007u << (3 * j) : 0u);
+        asm("" : "+s"(k.mask[j]));
+    }
+    return k;
+}
+
+template <int BITS>
+__device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv, const UnpackConsts& k) {
     if constexpr (BITS == 2) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -383,7 +405,7 @@ __device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int mm = m < 5 ? m : m - 5;
-                const uint32_t v = ((m < 5 ? w0 : w10) & (0x00030003u << (2 * mm))) | 0x64006400u;
+                const uint32_t v = ((m < 5 ? w0 : w10) & k.mask[mm]) | k.magic;
                 const _Float16 mul = (_Float16)(1.0f / (float)(1 << (2 * mm)));
                 const _Float16 add = (_Float16)(-(1024.0f / (float)(1 << (2 * mm)) + 2.0f));
                 lv[8 * h + m] = as_u32(__builtin_elementwise_fma(as_half2(v), half2_t{mul, mul}, half2_t{add, add}));
@@ -407,7 +429,7 @@ __device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv) {
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
                     if (j >= nj) continue;
-                    const uint32_t v = (X & (0x00070007u << (3 * j))) | 0x64006400u;
+                    const uint32_t v = (X & k.mask[j]) | k.magic;
                     const _Float16 mul = (_Float16)(1.0f / (float)(1 << (3 * j)));
                     const _Float16 add = (_Float16)(-(1024.0f / (float)(1 << (3 * j)) + 4.0f));
                     lv[8 * h + m0 + j] = as_u32(__builtin_elementwise_fma(as_half2(v), half2_t{mul, mul}, half2_t{add, add}));
@@ -469,6 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     const int L = m.n_layers, E = m.n_experts, D = m.d_model, F = m.d_ff, K = m.top_k;
     const int G = P.G, w = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const UnpackConsts uk = make_unpack_consts<BITS>();
     const int nkbD = D >> 5, nkbF = F >> 5, nch = F >> 4;
     const int PT = T * K;
     const int EPW = (E + G - 1) / G;
@@ -837,7 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
 #pragma unroll
                         for (int r = 0; r < 8; ++r) {
                             uint32_t lv[16];
-                            levels16<BITS>(q[a][r], lv);
+                            levels16<BITS>(q[a][r], lv, uk);
                             const float sc = kact ? h2f(sr[a][r]) : 0.0f;
 #pragma unroll
                             for (int t = 0; t < T; ++t)
@@ -916,7 +939,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         for (int k = 0; k < W; ++k) qv[k] = cw[(r * nkbF + kb) * W + k];
                         const float sc = h2f(sw[r * nkbF + kb]);
                         uint32_t lv[16];
-                        levels16<BITS>(qv, lv);
+                        levels16<BITS>(qv, lv, uk);
 #pragma unroll
                         for (int t = 0; t < T; ++t) {
                             const int pr = s_upair[u * T + t];
@@ -939,7 +962,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         for (int r = 0; r < 8; ++r) {
                             if (r0 + r >= nrows) continue;
                             uint32_t lv[16];
-                            levels16<BITS>(q[r], lv);
+                            levels16<BITS>(q[r], lv, uk);
                             const float sc = h2f(sr[r]);
 #pragma unroll
                             for (int t = 0; t < T; ++t) {
