@@ -693,16 +693,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
         }
         __syncthreads();
-        if (T == 1 && KPER >= 4 && 4 * K <= 64) {
+        constexpr bool kSplitTopk = T == 1 && KPER >= 4;
+        const bool split_topk = kSplitTopk && 4 * K <= 64;
+        if (split_topk) {
             // batch 1: each wave selects the top K of a quarter of the
-            // experts, then wave 0 merges the 4 K candidates
+            // experts, then wave 0 merges the 4 K candidates.  With one token
+            // the distinct experts are the selected ones in rank order; the
+            // gates are formed later, while the expert weight loads are in
+            // flight.
             constexpr int kq = KPER >= 4 ? KPER / 4 : 1;
             wave_topk_core<kq>(s_z, 64 * kq * wave, min(E, 64 * kq * (wave + 1)), K, s_cand_v + wave * K,
                                s_cand_i + wave * K, s_cand_k + wave * K);
             __syncthreads();
             if (wave == 0) {
                 wave_merge_topk(s_cand_v, s_cand_i, s_cand_k, 4 * K, K, s_cand_v + 64, s_cand_i + 64);
-                wave_gates(s_cand_v + 64, s_cand_i + 64, K, s_ids, s_gates);
+                if (lane < K) {
+                    const int e = s_cand_i[64 + lane];
+                    s_ids[lane] = e;
+                    s_uniq[lane] = e;
+                    s_upair[lane] = (short)lane;
+                }
+                if (lane == 0) s_misc[0] = K;
             }
         } else {
             for (int t = wave; t < T; t += 4) {
@@ -713,14 +724,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
         }
         __syncthreads();
-        if (w == 0 && P.ids_out) {
+        // gates of the batch-1 path (wave 0), and the routing outputs
+        auto finish_gates = [&]() {
+            if constexpr (kSplitTopk) {
+                wave_gates(s_cand_v + 64, s_cand_i + 64, K, s_ids, s_gates);
+                if (w == 0 && P.ids_out && lane < K) {
+                    P.ids_out[(size_t)l * PT + lane] = s_cand_i[64 + lane];
+                    P.gates_out[(size_t)l * PT + lane] = s_gates[lane];
+                }
+            }
+        };
+        bool gates_pending = split_topk;
+        if (!split_topk && w == 0 && P.ids_out) {
             for (int i = tid; i < PT; i += kThreads) {
                 P.ids_out[(size_t)l * PT + i] = s_ids[i];
                 P.gates_out[(size_t)l * PT + i] = s_gates[i];
             }
         }
         // distinct experts of the batch, in slot order of first appearance
-        if (PT <= 64) {
+        if (split_topk) {
+            // set above
+        } else if (PT <= 64) {
             if (wave == 0) {
                 // lane p holds pair p; its expert's first pair is the lowest q
                 // with the same id; first pairs are numbered by a ballot
@@ -844,6 +868,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                             sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
                         }
                     }
+                    if (gates_pending) {
+                        gates_pending = false;
+                        if (wave == 0) finish_gates();
+                    }
                     uint32_t xpk[T][16];
                     if (kb0 > 0) {
 #pragma unroll
@@ -899,6 +927,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 __syncthreads();
             }
         }
+        if (gates_pending && wave == 0) finish_gates();   // workgroups without gate/up items
         // the copies must have landed before any wave reads them after the barrier
         if (!grid_barrier(P, ++epoch, &s_misc[1], [&]() {
                 issue_down_prefetch();
