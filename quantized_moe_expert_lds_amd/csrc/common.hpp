@@ -16,10 +16,6 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxDModel = 16384;
 constexpr int kMaxDff = 4096;
 
-// router, large-batch path: 64 tokens x 64 experts per workgroup, 32-row k-steps
-constexpr int kRouteTileT = 64;
-constexpr int kRouteTileE = 64;
-constexpr int kRouteTileD = 32;
 // bucketing: pairs per block
 constexpr int kBucketBlock = 256;
 // prefill grouped GEMM tile

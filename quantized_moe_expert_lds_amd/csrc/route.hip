@@ -13,11 +13,12 @@
 //    128-bit loads and produces complete logits; a second small kernel (one
 //    wavefront per token) selects the top-k.  No cross-workgroup
 //    synchronisation inside a kernel.
-//  * large batches (prefill): a tiled fp64 GEMM in which every logit is
-//    accumulated by one thread over d in ascending order with fused
-//    multiply-adds (each fp32 x fp32 product is exact in fp64, so this is the
-//    same rounding sequence as the plain definition), then one wavefront per
-//    token selects the top-k.
+//  * large batches (prefill): an fp64 GEMM on the matrix cores
+//    (v_mfma_f64_16x16x4_f64) in which every logit is accumulated over d in
+//    ascending order, one fused multiply-add per d (each fp32 x fp32 product
+//    is exact in fp64, so this is the same rounding sequence as the plain
+//    definition; a GPU test checks the logits bit for bit), then one
+//    wavefront per token selects the top-k.
 #include "common.hpp"
 
 #include <math.h>
@@ -87,61 +88,108 @@ __global__ __launch_bounds__(256) void route_logits_kernel(moe_router_t r, const
 }
 
 // ---------------------------------------------------------------- large T
-// grid: (ceil(E/64), ceil(T/64)), block 256: thread (ty = tid/16, tx = tid%16)
-// owns tokens t0 + 4 ty .. +3 and experts e0 + 4 tx .. +3.
-__global__ __launch_bounds__(256) void route_gemm_kernel(moe_router_t r, const void* __restrict__ x,
-                                                         int x_bf16, int T, double* __restrict__ z) {
-    const int E = r.n_experts, D = r.d_model;
-    const int e0 = blockIdx.x * kRouteTileE, t0 = blockIdx.y * kRouteTileT;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    __shared__ double xs[kRouteTileD][kRouteTileT + 2];
-    __shared__ double ws_[kRouteTileD][kRouteTileE + 2];
+// fp64 matrix cores (v_mfma_f64_16x16x4_f64).  A block of 256 threads
+// computes a 128-token x 64-expert tile of z; d runs in chunks of 32 through
+// LDS, where x and w sit as fp64, transposed ([d][token], [d][expert]) so a
+// fragment read is 16 consecutive doubles.  Wave v owns tokens
+// 64 (v & 1) .. +64 and experts 32 (v >> 1) .. +32: 4 x 2 MFMA tiles, each
+// accumulating over d in ascending groups of 4.  The next chunk is loaded
+// into registers while the current one multiplies.
+typedef double double4_t __attribute__((ext_vector_type(4)));
+constexpr int kR64T = 128, kR64E = 64, kR64K = 32;
 
-    double acc[4][4];
+__global__ __launch_bounds__(256, 2) void route_gemm_kernel(moe_router_t r, const void* __restrict__ x,
+                                                            int x_bf16, int T, double* __restrict__ z) {
+    const int E = r.n_experts, D = r.d_model;
+    const int e0 = blockIdx.x * kR64E, t0 = blockIdx.y * kR64T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wt = 64 * (wave & 1), we = 32 * (wave >> 1);
+    __shared__ double xs[kR64K][kR64T + 1];
+    __shared__ double ws_[kR64K][kR64E + 1];
+
+    // staging: float4 f = tid + 256 i of a chunk holds d 4 (f & 7) .. +3 of
+    // token (or expert) f >> 3
+    float4 xr[4], wr[2];
+    auto load = [&](int d0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f = tid + 256 * i, t = t0 + (f >> 3), d = d0 + 4 * (f & 7);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < T) {
+                const size_t o = (size_t)t * D + d;
+                if (x_bf16) {
+                    const uint2 b = *reinterpret_cast<const uint2*>((const uint16_t*)x + o);
+                    v = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                                    __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+                } else {
+                    v = *reinterpret_cast<const float4*>((const float*)x + o);
+                }
+            }
+            xr[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int f = tid + 256 * i, e = e0 + (f >> 3), d = d0 + 4 * (f & 7);
+            wr[i] = e < E ? *reinterpret_cast<const float4*>(r.w + (size_t)e * D + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f = tid + 256 * i, t = f >> 3, dd = 4 * (f & 7);
+            xs[dd][t] = xr[i].x;
+            xs[dd + 1][t] = xr[i].y;
+            xs[dd + 2][t] = xr[i].z;
+            xs[dd + 3][t] = xr[i].w;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int f = tid + 256 * i, e = f >> 3, dd = 4 * (f & 7);
+            ws_[dd][e] = wr[i].x;
+            ws_[dd + 1][e] = wr[i].y;
+            ws_[dd + 2][e] = wr[i].z;
+            ws_[dd + 3][e] = wr[i].w;
+        }
+    };
+
+    double4_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-
-    for (int d0 = 0; d0 < D; d0 += kRouteTileD) {
-        // x tile: 64 tokens x 32 d -> transposed into xs[d][t]
-        for (int i = tid; i < kRouteTileT * kRouteTileD; i += 256) {
-            const int t = i / kRouteTileD, dd = i % kRouteTileD;
-            const int tt = t0 + t, d = d0 + dd;
-            xs[dd][t] = (tt < T && d < D) ? load_x(x, x_bf16, (size_t)tt * D + d) : 0.0;
-        }
-        for (int i = tid; i < kRouteTileD * kRouteTileE; i += 256) {
-            const int ee = i / kRouteTileD, dd = i % kRouteTileD;
-            const int d = d0 + dd, e = e0 + ee;
-            ws_[dd][ee] = (d < D && e < E) ? (double)r.w[(size_t)e * D + d] : 0.0;
-        }
+        for (int j = 0; j < 2; ++j) acc[i][j] = double4_t{0.0, 0.0, 0.0, 0.0};
+    load(0);
+    for (int d0 = 0; d0 < D; d0 += kR64K) {
+        store();
         __syncthreads();
-#pragma unroll 4
-        for (int dd = 0; dd < kRouteTileD; ++dd) {
-            double xv[4], wv[4];
+        load(min(d0 + kR64K, D - kR64K));                // the last reload is unused
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = xs[dd][4 * ty + i];
+        for (int kk = 0; kk < kR64K / 4; ++kk) {
+            const int k = 4 * kk + (lane >> 4);
+            double a[4], b[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wv[j] = ws_[dd][4 * tx + j];
+            for (int i = 0; i < 4; ++i) a[i] = xs[k][wt + 16 * i + (lane & 15)];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = ws_[k][we + 16 * j + (lane & 15)];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(xv[i], wv[j], acc[i][j]);
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
+    // lane l holds rows (l >> 4) + 4 v, v = 0..3, of column l & 15 of each tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * ty + i;
-        if (t >= T) continue;
+    for (int j = 0; j < 2; ++j) {
+        const int e = e0 + we + 16 * j + (lane & 15);
+        if (e >= E) continue;
+        const double bias = r.bias ? (double)r.bias[e] : 0.0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + 4 * tx + j;
-            if (e >= E) continue;
-            double s = acc[i][j];
-            if (r.bias) s += (double)r.bias[e];
-            z[(size_t)t * E + e] = s;
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + wt + 16 * i + (lane >> 4) + 4 * v;
+                if (t < T) z[(size_t)t * E + e] = r.bias ? acc[i][j][v] + bias : acc[i][j][v];
+            }
     }
 }
 
@@ -178,7 +226,7 @@ hipError_t launch_route_small(const moe_router_t& r, const void* x, int x_bf16, 
 hipError_t launch_route_large(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
                               float* gates, char* ws, const RouteWs& L, hipStream_t s) {
     double* z = (double*)(ws + L.zfull);
-    dim3 grid(cdiv(r.n_experts, kRouteTileE), cdiv(T, kRouteTileT));
+    dim3 grid(cdiv(r.n_experts, kR64E), cdiv(T, kR64T));
     route_gemm_kernel<<<grid, 256, 0, s>>>(r, x, x_bf16, T, z);
     topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(z, T, r.n_experts, r.top_k, ids, gates);
     return hipGetLastError();

@@ -339,6 +339,27 @@ def test_prefill_chunk_8192(q, full1):
     assert torch.isfinite(y).all()
 
 
+def test_route_logits_bit_exact_8192(q, full1):
+    _say("moe_route, 8,192 tokens: fp64 logits bit for bit against the ascending-d definition (sampled tokens)")
+    wl = mi.WORKLOADS["prefill_8192"]
+    _, layers, _, _ = full1
+    router, _ = layers[0]
+    T, K, E, D = wl.n_tokens, wl.top_k, wl.n_experts, wl.d_model
+    x = mi.activations_host(wl)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ws = q.workspace(q.MOE_OP_ROUTE, T, D, 0, E, K)
+    q.moe_route(router, xd, ids, w, None, None, ws)
+    torch.cuda.synchronize()
+    # the route workspace starts with the [T][E] fp64 logits (route_ws_layout)
+    z = ws[: T * E * 8].view(torch.float64).reshape(T, E).cpu().numpy()
+    wh, bh = mi.router_host(wl, 0)
+    sample = np.array([0, 1, 2, 3, 15, 16, 17, 127, 128, 1000, 4095, 4096, 6001, 8190, 8191])
+    z_o = O.router_logits(x[sample], wh, bh)
+    assert np.array_equal(z[sample], z_o), f"{np.mean(z[sample] != z_o):.3f} of the sampled logits differ"
+
+
 # ------------------------------------------------------------- errors
 
 def test_abi_errors(q, tiny):
