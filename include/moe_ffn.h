@@ -230,6 +230,35 @@ int moe_decode_stack(const moe_stack_t* model, const void* x, int x_dtype, int n
                      float* h_out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Bytes of workspace moe_prefill_stack needs for `model` and chunks of at
+ * most chunk_tokens tokens (0 if the arguments are invalid).  It does not
+ * depend on the prompt length. */
+size_t moe_prefill_stack_workspace_size(const moe_stack_t* model, int chunk_tokens);
+
+/* Chunked prefill of a prompt through every layer of a stack, the way the
+ * pages process long prompts (chunks of up to 8,192 tokens; bnskd, section
+ * 工程细节).  The prompt is cut into chunks of chunk_tokens tokens (the last
+ * may be shorter); each chunk runs through all layers before the next one
+ * starts:
+ *   h_0 = x;  for l = 0 .. L-1:
+ *     u_l = h_l if l == 0, else moe_residual_rmsnorm's u of h_l
+ *     ids_l, gates_l, buckets_l = moe_route(layer l, u_l)
+ *     h_{l+1} = h_l + moe_ffn_prefill(layer l, u_l, gates_l, buckets_l)
+ *   h_out = h_L
+ * Tokens do not interact, so a token's result does not depend on the chunk
+ * size; each layer matches moe_route and moe_ffn_prefill called one by one.
+ * Work is enqueued on `stream` as one sequence of kernel launches per
+ * (chunk, layer); nothing synchronises.
+ *
+ *   x     device [n_tokens][d_model], fp32 or bf16
+ *   h_out device fp32 [n_tokens][d_model] (output; also the residual stream)
+ *   ws    device scratch of moe_prefill_stack_workspace_size(model,
+ *         chunk_tokens) bytes, 256-byte aligned; holds no state between calls
+ * Supported: bits == 2, d_model a multiple of 256, d_ff a multiple of 128,
+ * the moe_route limits on n_experts and top_k, chunk_tokens * top_k <= 2^28. */
+int moe_prefill_stack(const moe_stack_t* model, const void* x, int x_dtype, int n_tokens, int chunk_tokens,
+                      double eps, float* h_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Static English text for a status code. */
 const char* moe_status_string(int status);
 

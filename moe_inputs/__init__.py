@@ -221,6 +221,9 @@ WORKLOADS = {
         # stack of such layers is a shape variant for the tests
         Workload("coder_256", FAMILY_CODER, 4, 256, 2048, 768, 10, 2, 2, "f32", True, True, act_tag=6,
                  note="4 layers x 256 experts, 2 tokens, 2-bit"),
+        # a prompt cut into chunks through a short stack of tiny layers
+        Workload("tiny_stack", FAMILY_TINY, 3, 16, 256, 128, 2, 40, 2, "f32", True, True, act_tag=7,
+                 note="3 layers x 16 experts, 40 tokens, chunked prefill"),
     ]
 }
 

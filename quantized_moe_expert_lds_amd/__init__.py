@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
     "MOE_F32", "MOE_BF16", "MOE_OP_ROUTE", "MOE_OP_DECODE", "MOE_OP_PREFILL", "moe_stack_workspace_size",
-    "stack_workspace",
+    "stack_workspace", "moe_prefill_stack_workspace_size", "prefill_stack_workspace", "moe_prefill_stack",
     "MOE_STACK_ERROR_OFFSET", "MoeError", "Router", "Experts", "Stack", "lib_path", "library",
     "moe_workspace_size", "workspace", "moe_route", "moe_ffn_decode", "moe_ffn_prefill", "moe_decode_stack",
     "moe_residual_rmsnorm", "moe_status_string", "EXPORTED_SYMBOLS",
@@ -30,7 +30,8 @@ MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
 MOE_STACK_ERROR_OFFSET = 2304
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_ffn_decode", "moe_ffn_prefill",
-                    "moe_stack_workspace_size", "moe_decode_stack", "moe_residual_rmsnorm", "moe_status_string")
+                    "moe_stack_workspace_size", "moe_decode_stack", "moe_prefill_stack_workspace_size",
+                    "moe_prefill_stack", "moe_residual_rmsnorm", "moe_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "lib", "libmoe_ffn.so")
@@ -79,6 +80,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_stack_workspace_size.restype = Z
     lib.moe_decode_stack.argtypes = [ctypes.POINTER(_StackT), P, I, I, D, P, P, P, P, Z, P]
     lib.moe_decode_stack.restype = I
+    lib.moe_prefill_stack_workspace_size.argtypes = [ctypes.POINTER(_StackT), I]
+    lib.moe_prefill_stack_workspace_size.restype = Z
+    lib.moe_prefill_stack.argtypes = [ctypes.POINTER(_StackT), P, I, I, I, D, P, P, Z, P]
+    lib.moe_prefill_stack.restype = I
     lib.moe_residual_rmsnorm.argtypes = [P, P, P, I, I, D, P]
     lib.moe_residual_rmsnorm.restype = I
     lib.moe_status_string.argtypes = [I]
@@ -272,6 +277,26 @@ def moe_decode_stack(stack: Stack, x: torch.Tensor, h_out: torch.Tensor, ws: Opt
                                   _ptr(topk_ids), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream))
     _check("moe_decode_stack", st)
+
+
+def moe_prefill_stack_workspace_size(stack: Stack, chunk_tokens: int) -> int:
+    return int(library.moe_prefill_stack_workspace_size(ctypes.byref(stack._c), chunk_tokens))
+
+
+def prefill_stack_workspace(stack: Stack, chunk_tokens: int, device="cuda") -> torch.Tensor:
+    """A workspace for moe_prefill_stack (it keeps no state between calls)."""
+    n = moe_prefill_stack_workspace_size(stack, chunk_tokens)
+    if n == 0:
+        raise MoeError("moe_prefill_stack_workspace_size", MOE_ERR_ARG)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_prefill_stack(stack: Stack, x: torch.Tensor, h_out: torch.Tensor, chunk_tokens: int,
+                      ws: Optional[torch.Tensor], eps: float = 1e-6, stream=None) -> None:
+    st = library.moe_prefill_stack(ctypes.byref(stack._c), _ptr(x), _dtype(x), x.shape[0], int(chunk_tokens),
+                                   float(eps), _ptr(h_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(stream))
+    _check("moe_prefill_stack", st)
 
 
 def moe_residual_rmsnorm(h: torch.Tensor, y: Optional[torch.Tensor], u: torch.Tensor, eps: float = 1e-6,

@@ -208,6 +208,75 @@ int moe_residual_rmsnorm(float* h, const float* y, float* u, int n_tokens, int d
     return hip_status(launch_residual_rmsnorm(h, y, u, n_tokens, d, eps, (hipStream_t)stream));
 }
 
+size_t moe_prefill_stack_workspace_size(const moe_stack_t* m, int chunk_tokens) {
+    if (!m || chunk_tokens <= 0 || m->n_layers <= 0 || m->n_experts <= 0 || m->d_model <= 0 || m->d_ff <= 0 ||
+        m->top_k <= 0)
+        return 0;
+    return prefill_stack_ws_layout(chunk_tokens, m->d_model, m->d_ff, m->n_experts, m->top_k).total;
+}
+
+int moe_prefill_stack(const moe_stack_t* m, const void* x, int x_dtype, int n_tokens, int chunk_tokens, double eps,
+                      float* h_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!m || !x || !h_out || n_tokens <= 0 || chunk_tokens <= 0 || !(eps >= 0.0)) return MOE_ERR_ARG;
+    if (!m->router_w || !m->gate_q || !m->up_q || !m->down_q || !m->gate_s || !m->up_s || !m->down_s)
+        return MOE_ERR_ARG;
+    const int xf = dtype_flag(x_dtype);
+    if (xf < 0) return MOE_ERR_ARG;
+    const int L = m->n_layers, E = m->n_experts, D = m->d_model, F = m->d_ff, K = m->top_k;
+    if (L <= 0 || E <= 0 || D <= 0 || F <= 0 || K <= 0) return MOE_ERR_ARG;
+    if (m->bits != 2 || D % kDownBN || F % kGateUpBN || D > kMaxDModel || F > kMaxDff || E > kMaxExperts ||
+        K > E || K > kMaxTopK)
+        return MOE_ERR_UNSUPPORTED;
+    if ((long long)chunk_tokens * K > (1LL << 28)) return MOE_ERR_UNSUPPORTED;
+    const PrefillStackWs W = prefill_stack_ws_layout(chunk_tokens, D, F, E, K);
+    int st = check_ws(ws, ws_bytes, W.total);
+    if (st) return st;
+    if ((st = check_device())) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* b = (char*)ws;
+    int32_t* ids = (int32_t*)(b + W.ids);
+    float* gates = (float*)(b + W.gates);
+    int32_t* offsets = (int32_t*)(b + W.offsets);
+    int32_t* pairs = (int32_t*)(b + W.pairs);
+    float* y = (float*)(b + W.y);
+    float* u = (float*)(b + W.u);
+    const size_t x_row = (size_t)D * (xf ? 2 : 4);
+    const size_t gu_words = (size_t)E * F * (D / 32) * 2, d_words = (size_t)E * D * (F / 32) * 2;
+    const size_t gu_blocks = (size_t)E * F * (D / 32), d_blocks = (size_t)E * D * (F / 32);
+    // chunk-major: every chunk passes through all layers before the next starts
+    for (int c0 = 0; c0 < n_tokens; c0 += chunk_tokens) {
+        const int Tc = n_tokens - c0 < chunk_tokens ? n_tokens - c0 : chunk_tokens;
+        const void* xc = (const char*)x + (size_t)c0 * x_row;
+        float* h = h_out + (size_t)c0 * D;
+        hipError_t e = launch_to_f32(xc, xf, (size_t)Tc * D, h, s);
+        for (int l = 0; l < L && e == hipSuccess; ++l) {
+            const moe_router_t r{D, E, K, m->router_w + (size_t)l * E * D, m->router_b ? m->router_b + (size_t)l * E : nullptr};
+            moe_experts_t ex{};
+            ex.n_experts = E;
+            ex.d_model = D;
+            ex.d_ff = F;
+            ex.bits = 2;
+            ex.gate_q = m->gate_q + l * gu_words;
+            ex.up_q = m->up_q + l * gu_words;
+            ex.down_q = m->down_q + l * d_words;
+            ex.gate_s = m->gate_s + l * gu_blocks;
+            ex.up_s = m->up_s + l * gu_blocks;
+            ex.down_s = m->down_s + l * d_blocks;
+            const void* ul = l == 0 ? xc : (const void*)u;
+            const int uf = l == 0 ? xf : 0;
+            e = Tc <= kMaxDecodeTokens ? launch_route_small(r, ul, uf, Tc, ids, gates, b + W.route, W.rl, s)
+                                       : launch_route_large(r, ul, uf, Tc, ids, gates, b + W.route, W.rl, s);
+            if (e == hipSuccess) e = launch_buckets(ids, Tc, K, E, offsets, pairs, b + W.route, W.rl, s);
+            if (e == hipSuccess)
+                e = launch_prefill(ex, ul, uf, Tc, gates, K, offsets, pairs, y, b + W.prefill, W.pl, s);
+            // h += y; u = RMSNorm(h), the next layer's input
+            if (e == hipSuccess) e = launch_residual_rmsnorm(h, y, u, Tc, D, eps, s);
+        }
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
 const char* moe_status_string(int status) {
     switch (status) {
         case MOE_OK: return "ok";

@@ -62,6 +62,14 @@ inline RouteWs route_ws_layout(int T, int D, int E, int K) {
     return w;
 }
 
+// chunked prefill through a stack: per-chunk buffers, then the route and
+// prefill workspaces of one chunk
+struct PrefillStackWs {
+    size_t ids, gates, offsets, pairs, y, u, route, prefill, total;
+    RouteWs rl;
+    PrefillWs pl;
+};
+
 inline DecodeWs decode_ws_layout(int T, int F, int K) {
     DecodeWs w{};
     w.h = 0;
@@ -93,6 +101,32 @@ inline PrefillWs prefill_ws_layout(int T, int D, int F, int E, int K) {
     return w;
 }
 
+inline PrefillStackWs prefill_stack_ws_layout(int Tc, int D, int F, int E, int K) {
+    PrefillStackWs w{};
+    const size_t P = (size_t)Tc * K;
+    size_t off = 0;
+    w.ids = off;
+    off += align256(sizeof(int32_t) * P);
+    w.gates = off;
+    off += align256(sizeof(float) * P);
+    w.offsets = off;
+    off += align256(sizeof(int32_t) * ((size_t)E + 1));
+    w.pairs = off;
+    off += align256(sizeof(int32_t) * P);
+    w.y = off;
+    off += align256(sizeof(float) * (size_t)Tc * D);
+    w.u = off;
+    off += align256(sizeof(float) * (size_t)Tc * D);
+    w.rl = route_ws_layout(Tc, D, E, K);
+    w.route = off;
+    off += w.rl.total;
+    w.pl = prefill_ws_layout(Tc, D, F, E, K);
+    w.prefill = off;
+    off += w.pl.total;
+    w.total = off;
+    return w;
+}
+
 // -------------------------------------------------------- kernel launchers
 // Each returns hipGetLastError() of its launches.
 hipError_t launch_route_small(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
@@ -111,6 +145,7 @@ hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, 
                                hipStream_t s);
 hipError_t launch_residual_rmsnorm(float* h, const float* y, float* u, int T, int d, double eps,
                                    hipStream_t s);
+hipError_t launch_to_f32(const void* x, int x_bf16, size_t n, float* out, hipStream_t s);
 
 }  // namespace qmoe
 

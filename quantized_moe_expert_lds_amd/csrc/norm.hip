@@ -34,9 +34,22 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(float* __restrict
     for (int i = tid; i < d; i += 256) ur[i] = (float)((double)hr[i] / r);
 }
 
+// x (fp32 or bf16) -> fp32, the first residual of a chunk
+__global__ __launch_bounds__(256) void to_f32_kernel(const void* __restrict__ x, int x_bf16, size_t n,
+                                                     float* __restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    out[i] = x_bf16 ? __uint_as_float((uint32_t)((const uint16_t*)x)[i] << 16) : ((const float*)x)[i];
+}
+
 }  // namespace
 
 namespace qmoe {
+
+hipError_t launch_to_f32(const void* x, int x_bf16, size_t n, float* out, hipStream_t s) {
+    to_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, x_bf16, n, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_residual_rmsnorm(float* h, const float* y, float* u, int T, int d, double eps, hipStream_t s) {
     residual_rmsnorm_kernel<<<T, 256, 0, s>>>(h, y, u, d, eps);
