@@ -59,14 +59,15 @@ def build_stack(q, torch, wl, bits=None):
     return st, (ex, rw, rb)
 
 
-def bench_stack(q, torch, wl, steps, warmup, bits=None):
+def bench_stack(q, torch, wl, steps, warmup, bits=None, built=None):
     """Time `steps` decode steps (one moe_decode_stack launch each, a new
     token batch per step) after `warmup` steps.  Returns wall seconds per step,
     the average kernel duration from HIP events on the launch stream, and the
     algorithmic HBM bytes per launch (packed codes + scales of the distinct
-    experts each layer selects, the router matrices, activations)."""
+    experts each layer selects, the router matrices, activations).  `built`
+    is a (Stack, tensors) pair from build_stack to reuse; it is not freed."""
     import moe_inputs.gpu as g
-    st, keep = build_stack(q, torch, wl, bits)
+    st, keep = build_stack(q, torch, wl, bits) if built is None else built
     T, L, K, D, E = wl.n_tokens, st.n_layers, wl.top_k, wl.d_model, wl.n_experts
     n_tok = steps + warmup
     xs = torch.stack([g.activations(wl, stream=s) for s in range(n_tok)])
@@ -96,9 +97,46 @@ def bench_stack(q, torch, wl, steps, warmup, bits=None):
     per_expert = 3 * D * wl.d_ff // 32 * (4 * (2 if bits_ == 2 else 3) + 2)
     nbytes = float(uniq.sum(axis=1).mean()) * per_expert + L * E * D * 4 + (E * 4 * L if wl.zipf_bias else 0) \
         + 2 * T * D * 4
-    del st, keep, xs, ws
+    del xs, ws
+    if built is None:
+        del st, keep
     torch.cuda.empty_cache()
     return wall, kern, nbytes, float(uniq.mean())
+
+
+def bench_prefill_stack(q, torch, st, steps=2, warmup=1):
+    """A 32,768-token prompt in 4 chunks of 8,192 through every layer of the
+    48-layer stack (moe_prefill_stack: router, buckets, expert FFN, residual +
+    RMSNorm per chunk and layer)."""
+    import moe_inputs as mi
+    import moe_inputs.gpu as g
+    wl = mi.WORKLOADS["prefill_8192"]
+    chunk = wl.n_tokens
+    T = 4 * chunk
+    x = torch.cat([g.activations(wl, stream=s) for s in range(4)])
+    h = torch.empty((T, st.d_model), device="cuda")
+    ws = q.prefill_stack_workspace(st, chunk)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        q.moe_prefill_stack(st, x, h, chunk, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        q.moe_prefill_stack(st, x, h, chunk, ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    gpu_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    L, K, D, F = st.n_layers, st.top_k, st.d_model, wl.d_ff
+    flops = 2.0 * T * K * 3 * D * F * L
+    res = {"workload": "prefill_32k_48layer", "tokens": T, "chunk": chunk, "layers": L,
+           "tokens_per_s": T / wall, "ms_per_prompt": wall * 1e3, "gpu_ms_per_prompt": gpu_s * 1e3,
+           "ffn_tflops_incl_routing": flops / gpu_s / 1e12}
+    del x, h, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(n_layers_sample=12):
@@ -258,11 +296,17 @@ def main():
         return
     wl = mi.WORKLOADS["decode_48layer"]
     log("48-layer decode, batch 1: generating 48 x 512 experts in HBM and timing")
-    dt, kern, nbytes, uniq = bench_stack(q, torch, wl, args.steps, args.warmup)
+    built = build_stack(q, torch, wl)
+    dt, kern, nbytes, uniq = bench_stack(q, torch, wl, args.steps, args.warmup, built=built)
     achieved = nbytes / kern / 1e9
     log(f"decode step {dt * 1e6:.1f} us wall, kernel {kern * 1e6:.1f} us, {achieved:.0f} GB/s")
 
     also = {}
+    if not args.no_also:
+        log("prefill of a 32,768-token prompt through the 48 layers")
+        also["prefill_stack"] = bench_prefill_stack(q, torch, built[0])
+    del built
+    torch.cuda.empty_cache()
     if not args.no_also:
         log("prefill 8192")
         also["prefill"] = bench_prefill(q, torch)
