@@ -279,6 +279,8 @@ def main():
     ap.add_argument("--no-also", action="store_true", help="skip the prefill and verify workloads")
     ap.add_argument("--profile-pass", action="store_true",
                     help="only 3 decode steps and a calibration copy, for rocprofv3 counter passes")
+    ap.add_argument("--prefill-pass", action="store_true",
+                    help="only the 8,192-token prefill chunk (3 timed calls), for rocprofv3 passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE FFN path is built and measured on a single MI355X "
@@ -293,6 +295,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_pass:
         profile_pass(q, torch)
+        return
+    if args.prefill_pass:
+        print(json.dumps(bench_prefill(q, torch, steps=3, warmup=1)), flush=True)
         return
     wl = mi.WORKLOADS["decode_48layer"]
     log("48-layer decode, batch 1: generating 48 x 512 experts in HBM and timing")
