@@ -86,17 +86,23 @@ __global__ __launch_bounds__(kBucketBlock) void bucket_hist_kernel(const int32_t
     for (int i = tid; i < E; i += kBucketBlock) hist[(size_t)b * E + i] = h[i];
 }
 
-// one workgroup of 1024 threads; thread e owns expert column e
+// one workgroup of 1024 threads; thread e owns expert column e and walks it
+// in batches of 32 blocks whose loads are all in flight together
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(int* __restrict__ hist, int NB, int E, int P,
                                                            int32_t* __restrict__ offsets) {
     __shared__ int cnt[1024];
     const int tid = threadIdx.x;
     int run = 0;
     if (tid < E) {
-        for (int b = 0; b < NB; ++b) {
-            const int c = hist[(size_t)b * E + tid];
-            hist[(size_t)b * E + tid] = run;
-            run += c;
+        for (int b0 = 0; b0 < NB; b0 += 32) {
+            int c[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) c[i] = b0 + i < NB ? hist[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (b0 + i < NB) hist[(size_t)(b0 + i) * E + tid] = run;
+                run += c[i];
+            }
         }
     }
     cnt[tid] = run;
