@@ -110,15 +110,47 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
 }
 
 // Dequantise one 2-bit block (codes w0, w1; fp16 scale bits sb) into 16 fp16
-// pairs in unpack order: level * scale, exact in fp16.
-__device__ __forceinline__ void dequant_block2(uint32_t w0, uint32_t w1, uint16_t sb, uint32_t* out) {
-    const half2_t bias = {(_Float16)-1026.0f, (_Float16)-1026.0f};
+// pairs in unpack order: level * scale, exact in fp16.  Pair m < 8 of a word
+// holds its weights (m, m + 8), whose codes sit at bits 2m of the word's low
+// and high halves.  OR-ing the masked word (shifted by 10 for m >= 5, so the
+// bits stay inside the 10-bit mantissa) into 1024.0 gives 1024 + code * 4^m';
+// one fused multiply-add by 4^-m' and -(1024 * 4^-m' + 2) yields the level
+// exactly, and one multiply the scaled weight.  The mask and the magic are
+// kept in registers (DequantConsts) so the and-or is one v_and_or_b32: a
+// three-operand instruction takes no literal on gfx9.
+struct DequantConsts {
+    uint32_t magic;      // 0x64006400, in a VGPR
+    uint32_t mask[5];    // 0x00030003 << 2m', in SGPRs
+};
+
+__device__ __forceinline__ DequantConsts make_dequant_consts() {
+    DequantConsts k;
+    k.magic = 0x64006400u;
+    asm("" : "+v"(k.magic));
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        k.mask[j] = 0x00030003u << (2 * j);
+        asm("" : "+s"(k.mask[j]));
+    }
+    return k;
+}
+
+__device__ __forceinline__ void dequant_block2(uint32_t w0, uint32_t w1, uint16_t sb, uint32_t* out,
+                                               const DequantConsts& k) {
     const _Float16 s = __builtin_bit_cast(_Float16, sb);
     const half2_t s2 = {s, s};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        out[m] = as_u32((as_half2(codes2_pair(w0, 2 * m)) + bias) * s2);
-        out[8 + m] = as_u32((as_half2(codes2_pair(w1, 2 * m)) + bias) * s2);
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w = h ? w1 : w0, w10 = w >> 10;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int mm = m < 5 ? m : m - 5;
+            const uint32_t v = ((m < 5 ? w : w10) & k.mask[mm]) | k.magic;
+            const _Float16 mul = (_Float16)(1.0f / (float)(1 << (2 * mm)));
+            const _Float16 add = (_Float16)(-(1024.0f / (float)(1 << (2 * mm)) + 2.0f));
+            const half2_t lev = __builtin_elementwise_fma(as_half2(v), half2_t{mul, mul}, half2_t{add, add});
+            out[8 * h + m] = as_u32(lev * s2);
+        }
     }
 }
 
@@ -159,17 +191,17 @@ __device__ __forceinline__ void gemm_load(GemmStage& st, const uint16_t* const* 
 }
 
 __device__ __forceinline__ void gemm_store(const GemmStage& st, _Float16 (*As)[kLdsStride],
-                                           _Float16 (*Bs)[kLdsStride], int b_lds_row) {
+                                           _Float16 (*Bs)[kLdsStride], int b_lds_row, const DequantConsts& k) {
     const int tid = threadIdx.x;
     const int a_col = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[(tid >> 3) + 32 * i][a_col]) = st.a[i];
     uint32_t o[16];
     uint4* dst = reinterpret_cast<uint4*>(&Bs[b_lds_row][0]);
-    dequant_block2(st.b.x, st.b.y, (uint16_t)(st.s & 0xffff), o);
+    dequant_block2(st.b.x, st.b.y, (uint16_t)(st.s & 0xffff), o, k);
 #pragma unroll
     for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-    dequant_block2(st.b.z, st.b.w, (uint16_t)(st.s >> 16), o);
+    dequant_block2(st.b.z, st.b.w, (uint16_t)(st.s >> 16), o, k);
 #pragma unroll
     for (int q = 0; q < 4; ++q) dst[4 + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
 }
@@ -180,10 +212,11 @@ __device__ __forceinline__ void gemm_kloop(const uint16_t* const* a_src, const u
                                            _Float16 (*As)[kLdsStride], _Float16 (*Bs)[kLdsStride],
                                            float4_t (&acc)[4][8]) {
     const int lane = threadIdx.x & 63;
+    const DequantConsts dk = make_dequant_consts();
     GemmStage st;
     gemm_load(st, a_src, b_q, b_s, 0);
     for (int ks = 0; ks < nsteps; ++ks) {
-        gemm_store(st, As, Bs, b_lds_row);
+        gemm_store(st, As, Bs, b_lds_row, dk);
         __syncthreads();
         gemm_load(st, a_src, b_q, b_s, min(ks + 1, nsteps - 1));   // the last reload is unused
 #pragma unroll
