@@ -206,7 +206,11 @@ __device__ __forceinline__ void gemm_store(const GemmStage& st, _Float16 (*As)[k
     for (int q = 0; q < 4; ++q) dst[4 + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
 }
 
-// the K loop shared by both GEMMs; ni = 16-row slices of the wave that hold pairs
+// the K loop shared by both GEMMs; ni = 16-row slices of the wave that hold
+// pairs.  Full tiles (ni == 4) take a copy without the per-slice branches, so
+// the MFMAs of a step form one block the scheduler can interleave with the
+// fragment reads.
+template <bool kFull>
 __device__ __forceinline__ void gemm_kloop(const uint16_t* const* a_src, const uint32_t* b_q, const uint16_t* b_s,
                                            int b_lds_row, int nsteps, int wm, int wn, int ni,
                                            _Float16 (*As)[kLdsStride], _Float16 (*Bs)[kLdsStride],
@@ -229,7 +233,7 @@ __device__ __forceinline__ void gemm_kloop(const uint16_t* const* a_src, const u
             for (int j = 0; j < 8; ++j) b[j] = lds_frag(&Bs[128 * wn + 16 * j + (lane & 15)][kofs]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (i >= ni) continue;                      // slice beyond the bucket
+                if (!kFull && i >= ni) continue;            // slice beyond the bucket
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -283,7 +287,8 @@ __global__ __launch_bounds__(256, 2) void gemm_gateup_kernel(moe_experts_t ex, c
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-    gemm_kloop(a_src, b_q, b_s, b_lds_row, D / kGemmBK, wm, wn, ni, As, Bs, acc);
+    if (ni == 4) gemm_kloop<true>(a_src, b_q, b_s, b_lds_row, D / kGemmBK, wm, wn, ni, As, Bs, acc);
+    else gemm_kloop<false>(a_src, b_q, b_s, b_lds_row, D / kGemmBK, wm, wn, ni, As, Bs, acc);
 
     // epilogue: h = silu(g) * u -> fp16, stored in bucket-row order, each
     // 32-block of d_ff in unpack pair order
@@ -340,7 +345,8 @@ __global__ __launch_bounds__(256, 2) void gemm_down_kernel(moe_experts_t ex, con
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-    gemm_kloop(a_src, b_q, b_s, b_row, F / kGemmBK, wm, wn, ni, As, Bs, acc);
+    if (ni == 4) gemm_kloop<true>(a_src, b_q, b_s, b_row, F / kGemmBK, wm, wn, ni, As, Bs, acc);
+    else gemm_kloop<false>(a_src, b_q, b_s, b_row, F / kGemmBK, wm, wn, ni, As, Bs, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
