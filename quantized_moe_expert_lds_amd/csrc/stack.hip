@@ -897,6 +897,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         }
                     }
                 }
+                // wave sums, gathered so lane j = (a T + t) 4 + r holds the
+                // gate and up sums of (item a, token t, row r); one SwiGLU
+                // evaluation then covers all of them
+                static_assert(4 * T * kMaxItemsInFlight <= 64, "one lane per (item, token, row)");
+                float gv = 0.0f, uv = 0.0f;
 #pragma unroll
                 for (int a = 0; a < kMaxItemsInFlight; ++a) {
                     const int it = it0 + a * G;
@@ -908,8 +913,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                             if (!((tmask[a] >> t) & 1)) continue;
                             const float g = wave_sum_f32(acc[a][r][t]);
                             const float uu = wave_sum_f32(acc[a][4 + r][t]);
-                            if (lane == 0) s_hloc[(a * T + t) * 16 + 4 * wave + r] = silu_mul(g, uu);
+                            if (lane == (a * T + t) * 4 + r) {
+                                gv = g;
+                                uv = uu;
+                            }
                         }
+                }
+                {
+                    const int a = lane / (4 * T), t = (lane >> 2) % T, r = lane & 3;
+                    int tm = 0;
+#pragma unroll
+                    for (int b = 0; b < kMaxItemsInFlight; ++b)
+                        if (a == b && it0 + b * G < n_items) tm = tmask[b];
+                    const float hv = silu_mul(gv, uv);
+                    if (a < kMaxItemsInFlight && ((tm >> t) & 1)) s_hloc[(a * T + t) * 16 + 4 * wave + r] = hv;
                 }
                 __syncthreads();
                 if (tid < 8 * T * kMaxItemsInFlight) {
