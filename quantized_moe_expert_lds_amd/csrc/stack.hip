@@ -891,8 +891,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                             levels16<BITS>(q[a][r], lv, uk);
                             const float sc = kact ? h2f(sr[a][r]) : 0.0f;
 #pragma unroll
-                            for (int t = 0; t < T; ++t)
-                                if ((tmask[a] >> t) & 1)
+                            for (int t = 0; t < T; ++t)        // (one token: it chose every item's expert)
+                                if (T == 1 || ((tmask[a] >> t) & 1))
                                     acc[a][r][t] = fmaf(sc, dot16h(lv, kb0 == 0 ? xp0[t] : xpk[t]), acc[a][r][t]);
                         }
                     }
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     for (int r = 0; r < 4; ++r)
 #pragma unroll
                         for (int t = 0; t < T; ++t) {
-                            if (!((tmask[a] >> t) & 1)) continue;
+                            if (T > 1 && !((tmask[a] >> t) & 1)) continue;
                             const float g = wave_sum_f32(acc[a][r][t]);
                             const float uu = wave_sum_f32(acc[a][4 + r][t]);
                             if (lane == (a * T + t) * 4 + r) {
