@@ -19,8 +19,9 @@
 //           (ties to the lower id), derives the distinct experts of the batch
 //           and processes its share of (expert, 16-row d_ff chunk) items:
 //           2-/3-bit unpack, fp16 dot products with fp32 accumulation,
-//           SwiGLU, fp16 h per (token, slot) pair.  It also starts loading the
-//           down-projection rows it will need next.
+//           SwiGLU, fp16 h per (token, slot) pair.  While wave 0 waits at the
+//           next barrier, waves 1-3 copy the down-projection rows the
+//           workgroup needs next into LDS.
 //   DOWN  : workgroup w owns d_model rows w*DPW ..; it combines those rows of
 //           every distinct expert (blocks in order, slots in order with their
 //           gates), adds the residual and publishes its slice of h and its
