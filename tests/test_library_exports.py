@@ -76,3 +76,36 @@ def test_validation_before_any_device_call(lib):
     lib.moe_residual_rmsnorm.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                                                   ctypes.c_void_p]
     assert lib.moe_residual_rmsnorm(None, None, None, 1, 8, 1e-6, None) == -1
+
+
+def test_prefill_stack_validation_before_any_device_call(lib):
+    """moe_prefill_stack rejects bad arguments on the host: status codes
+    only, no pointer is dereferenced on the device."""
+    import quantized_moe_expert_lds_amd as q
+    P = ctypes.c_void_p
+    fake = P(256)          # never dereferenced: validation fails first
+    def stack(bits=2, d=2048, f=768, e=512, k=10, layers=2):
+        return q._StackT(layers, e, d, f, k, bits, fake, None, fake, fake, fake, fake, fake, fake)
+    call = lib.moe_prefill_stack
+    call.argtypes = [ctypes.POINTER(q._StackT), P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, P, P,
+                     ctypes.c_size_t, P]
+    call.restype = ctypes.c_int
+    size = lib.moe_prefill_stack_workspace_size
+    size.argtypes = [ctypes.POINTER(q._StackT), ctypes.c_int]
+    size.restype = ctypes.c_size_t
+    st = stack()
+    ok_args = lambda s, n=100, chunk=64, dtype=0: (ctypes.byref(s), fake, dtype, n, chunk, 1e-6, fake, fake,
+                                                   size(ctypes.byref(s), chunk), None)
+    assert size(ctypes.byref(st), 64) > 0
+    assert size(ctypes.byref(st), 0) == 0
+    assert size(None, 64) == 0
+    assert call(*ok_args(st, n=0)) == -1                      # no tokens
+    assert call(*ok_args(st, chunk=0)) == -1                  # no chunk
+    assert call(*ok_args(st, dtype=7)) == -1                  # unknown dtype
+    assert call(*ok_args(stack(bits=3))) == -2                # prefill GEMMs are 2-bit only
+    assert call(*ok_args(stack(d=2080))) == -2                # d_model not a multiple of 256
+    assert call(*ok_args(stack(f=800))) == -2                 # d_ff not a multiple of 128
+    assert call(*ok_args(stack(k=600, e=512))) == -2          # top_k > n_experts
+    args = list(ok_args(st))
+    args[8] = args[8] - 1                                     # workspace one byte short
+    assert call(*args) == -3
