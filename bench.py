@@ -143,10 +143,8 @@ def cpu_baseline(n_layers_sample=12):
     """The oracle (numpy) on the host cores: the first n layers of the 48-layer
     bs1 chain; expert generation (input preparation) is done before timing."""
     import moe_inputs as mi
+    from moe_inputs import host_cache
     import oracle.moe_oracle as O
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import helpers
-    import oracle_pool
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -161,11 +159,11 @@ def cpu_baseline(n_layers_sample=12):
     for l in range(n_layers_sample):
         u = h if l == 0 else O.rmsnorm(h)
         ids, _, _ = O.route(u, routers[l][0], routers[l][1], wl.top_k)
-        oracle_pool.prefetch(wl.name, l, np.unique(ids), wl.bits)
-        _, _, y = O.moe_layer(u, routers[l][0], routers[l][1], wl.top_k, helpers.oracle_experts(wl, l), wl.bits)
+        host_cache.prefetch(wl.name, l, np.unique(ids), wl.bits)
+        _, _, y = O.moe_layer(u, routers[l][0], routers[l][1], wl.top_k, host_cache.experts_of(wl, l), wl.bits)
         h = (h + y).astype(np.float32)
     t0 = time.perf_counter()
-    O.moe_chain(x, n_layers_sample, lambda l: routers[l], lambda l: helpers.oracle_experts(wl, l), wl.top_k,
+    O.moe_chain(x, n_layers_sample, lambda l: routers[l], lambda l: host_cache.experts_of(wl, l), wl.top_k,
                 wl.bits)
     dt = time.perf_counter() - t0
     per_token = dt * wl.n_layers / n_layers_sample

@@ -43,7 +43,15 @@
  * 2-bit: code = level + 2 (levels -2..1), weight i of a block in word i/16 at
  * bits [2(i mod 16), +2).  3-bit: code = level + 4 (levels -4..3), the three
  * words are one little-endian 96-bit string, weight i at bits [3i, 3i+3).
- * Dequantised weight = level * scale (exact in fp32).
+ * Dequantised weight = level * scale, exact in fp32 for every fp16 scale
+ * (the decode and stack paths apply the scale in fp32).  The prefill path
+ * feeds level * scale to the fp16 matrix cores, which is exact as long as it
+ * is representable in fp16: |level * scale| <= 65504, i.e. 2-bit scales up to
+ * 32752 (bits 0x77FF), which quantising any fp16-representable weights
+ * always gives; a larger scale makes a level -2 weight overflow to -inf in
+ * prefill only.  Subnormal and zero scales are exact on every path.  The
+ * SwiGLU intermediate h = silu(g) * u enters the down projection as fp16 on
+ * every path, so |h| must stay below 65504.
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
@@ -93,8 +101,8 @@ typedef struct {
 
 /* Stored experts of one layer (layout above).  All pointers device.
  * Supported: bits 2 or 3; d_model and d_ff multiples of 32, d_model <= 16384,
- * d_ff <= 4096.  Prefill additionally needs bits == 2, d_model % 128 == 0 and
- * d_ff % 64 == 0. */
+ * d_ff <= 4096.  Prefill additionally needs bits == 2, d_model % 256 == 0 and
+ * d_ff % 128 == 0. */
 typedef struct {
     int n_experts;
     int d_model;
@@ -224,11 +232,13 @@ size_t moe_stack_workspace_size(const moe_stack_t* model, int n_tokens);
  *   h_out        device fp32 [n_tokens][d_model] (output)
  *   topk_ids_out device int32 [L][n_tokens][top_k] or NULL (output)
  *   topk_w_out   device fp32  [L][n_tokens][top_k] or NULL (output; both or neither)
+ *   h_layers_out device fp32  [L][n_tokens][d_model] or NULL (output): h_{l+1}
+ *                after every layer l (its last row block equals h_out)
  * Supported: 1 <= n_tokens <= 8, d_model and d_ff multiples of 32 and
  * <= 4096, n_experts <= min(1024, 4 x compute units), top_k <= min(n_experts, 64). */
 int moe_decode_stack(const moe_stack_t* model, const void* x, int x_dtype, int n_tokens, double eps,
-                     float* h_out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                     void* stream);
+                     float* h_out, int32_t* topk_ids_out, float* topk_w_out, float* h_layers_out, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Bytes of workspace moe_prefill_stack needs for `model` and chunks of at
  * most chunk_tokens tokens (0 if the arguments are invalid).  It does not

@@ -178,12 +178,17 @@ def combine(gates: np.ndarray, outs: np.ndarray) -> np.ndarray:
     return y
 
 
-def moe_layer(x, router_w, router_b, k, expert_weights, bits):
+def moe_layer(x, router_w, router_b, k, expert_weights, bits, prepare=None):
     """One routed MoE FFN layer.
 
     ``expert_weights(e)`` returns the stored ((gate_q, gate_s), (up_q, up_s),
-    (down_q, down_s)) of expert e.  Returns (ids, gates, y fp32 [T][D])."""
+    (down_q, down_s)) of expert e.  ``prepare``, if given, is called once with
+    the distinct selected expert ids before any expert is requested (a hook
+    for fetching them in bulk; it takes no part in the arithmetic).
+    Returns (ids, gates, y fp32 [T][D])."""
     ids, gates, _ = route(x, router_w, router_b, k)
+    if prepare is not None:
+        prepare(np.unique(ids))
     xf = as_f32_activations(x)
     t = xf.shape[0]
     outs = np.zeros((t, k, xf.shape[1]), dtype=np.float32)
@@ -204,18 +209,21 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return (h64 / r).astype(np.float32)
 
 
-def moe_chain(x, n_layers, router_of, experts_of, k, bits, eps=1e-6):
+def moe_chain(x, n_layers, router_of, experts_of, k, bits, eps=1e-6, prepare_of=None):
     """Residual chain of MoE layers: h_0 = x; u_l = h_l for l = 0, else
     RMSNorm(h_l); h_{l+1} = h_l + MoE_l(u_l) (fp32 add).
 
-    ``router_of(l)`` -> (w, b); ``experts_of(l)`` -> callable e -> weights.
-    Returns (h_L, records) with one record (u, ids, gates, y) per layer."""
+    ``router_of(l)`` -> (w, b); ``experts_of(l)`` -> callable e -> weights;
+    ``prepare_of(l)``, if given, -> the ``prepare`` hook of ``moe_layer``.
+    Returns (h_L, records) with one record (u, ids, gates, y, h_{l+1}) per
+    layer."""
     h = as_f32_activations(x)
     recs = []
     for l in range(n_layers):
         u = h if l == 0 else rmsnorm(h, eps)
         w, b = router_of(l)
-        ids, gates, y = moe_layer(u, w, b, k, experts_of(l), bits)
-        recs.append((u, ids, gates, y))
+        ids, gates, y = moe_layer(u, w, b, k, experts_of(l), bits,
+                                  prepare=None if prepare_of is None else prepare_of(l))
         h = (h + y).astype(np.float32)
+        recs.append((u, ids, gates, y, h))
     return h, recs

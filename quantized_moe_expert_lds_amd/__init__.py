@@ -78,7 +78,7 @@ def _load() -> ctypes.CDLL:
     lib.moe_ffn_prefill.restype = I
     lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_StackT), I]
     lib.moe_stack_workspace_size.restype = Z
-    lib.moe_decode_stack.argtypes = [ctypes.POINTER(_StackT), P, I, I, D, P, P, P, P, Z, P]
+    lib.moe_decode_stack.argtypes = [ctypes.POINTER(_StackT), P, I, I, D, P, P, P, P, P, Z, P]
     lib.moe_decode_stack.restype = I
     lib.moe_prefill_stack_workspace_size.argtypes = [ctypes.POINTER(_StackT), I]
     lib.moe_prefill_stack_workspace_size.restype = Z
@@ -272,10 +272,10 @@ def stack_workspace(stack: Stack, n_tokens: int, device="cuda") -> torch.Tensor:
 
 def moe_decode_stack(stack: Stack, x: torch.Tensor, h_out: torch.Tensor, ws: Optional[torch.Tensor],
                      topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-                     eps: float = 1e-6, stream=None) -> None:
+                     eps: float = 1e-6, stream=None, h_layers: Optional[torch.Tensor] = None) -> None:
     st = library.moe_decode_stack(ctypes.byref(stack._c), _ptr(x), _dtype(x), x.shape[0], float(eps), _ptr(h_out),
-                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
-                                  _stream(stream))
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(h_layers), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream))
     _check("moe_decode_stack", st)
 
 

@@ -173,7 +173,8 @@ size_t moe_stack_workspace_size(const moe_stack_t* m, int n_tokens) {
 }
 
 int moe_decode_stack(const moe_stack_t* m, const void* x, int x_dtype, int n_tokens, double eps, float* h_out,
-                     int32_t* ids_out, float* gates_out, void* ws, size_t ws_bytes, void* stream) {
+                     int32_t* ids_out, float* gates_out, float* h_layers_out, void* ws, size_t ws_bytes,
+                     void* stream) {
     if (!m || !x || !h_out || n_tokens <= 0 || !(eps >= 0.0)) return MOE_ERR_ARG;
     if (!m->router_w || !m->gate_q || !m->up_q || !m->down_q || !m->gate_s || !m->up_s || !m->down_s)
         return MOE_ERR_ARG;
@@ -197,7 +198,8 @@ int moe_decode_stack(const moe_stack_t* m, const void* x, int x_dtype, int n_tok
     if ((E + G - 1) / G > 4 || (D + G - 1) / G > 32) return MOE_ERR_UNSUPPORTED;
     if (stack_lds_bytes(n_tokens, D, F, E, K, G, m->bits) > kStackLdsLimit)
         return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_decode_stack(*m, x, xf, n_tokens, h_out, ids_out, gates_out, eps, (char*)ws, Lw, G,
+    return hip_status(launch_decode_stack(*m, x, xf, n_tokens, h_out, ids_out, gates_out, h_layers_out, eps,
+                                          (char*)ws, Lw, G,
                                           (hipStream_t)stream));
 }
 

@@ -141,7 +141,7 @@ hipError_t launch_prefill(const moe_experts_t& ex, const void* x, int x_bf16, in
                           int K, const int32_t* offsets, const int32_t* pairs, float* y, char* ws,
                           const PrefillWs& L, hipStream_t s);
 hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, int T, float* h_out,
-                               int32_t* ids_out, float* gates_out, double eps, char* ws, const StackWs& L, int G,
+                               int32_t* ids_out, float* gates_out, float* h_layers, double eps, char* ws, const StackWs& L, int G,
                                hipStream_t s);
 hipError_t launch_residual_rmsnorm(float* h, const float* y, float* u, int T, int d, double eps,
                                    hipStream_t s);

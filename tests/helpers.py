@@ -5,6 +5,7 @@ from __future__ import annotations
 import numpy as np
 
 import moe_inputs as mi
+from moe_inputs import host_cache
 
 TOL = 2e-3          # max over rows of max|y_gpu - y_ref| / max|y_ref|
 
@@ -17,30 +18,23 @@ def row_rel_err(got, want) -> float:
     return float(np.max(num / den))
 
 
-_EXPERT_CACHE: dict = {}
+def floored_rel_err(got, want, floor=1e-3) -> float:
+    """Elementwise relative error with the denominator floored at
+    floor * max|want| of the row (near-zero outputs are not divided by ~0)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.maximum(np.abs(want), floor * np.max(np.abs(want), axis=-1, keepdims=True))
+    den = np.maximum(den, 1e-30)
+    return float(np.max(np.abs(got - want) / den))
 
 
 def host_expert(wl_name: str, layer: int, expert: int, bits: int):
     """Stored (gate, up, down) of one expert from the host generator."""
-    key = (wl_name, layer, expert, bits)
-    if key not in _EXPERT_CACHE:
-        wl = mi.WORKLOADS[wl_name]
-        _EXPERT_CACHE[key] = tuple(mi.expert_tensor_host(wl, layer, t, expert, bits)
-                                   for t in (mi.GATE, mi.UP, mi.DOWN))
-    return _EXPERT_CACHE[key]
-
-
-def host_expert_cache_put(key, value) -> None:
-    _EXPERT_CACHE[tuple(key)] = value
-
-
-def host_expert_cache_clear() -> None:
-    _EXPERT_CACHE.clear()
+    return host_cache.expert(wl_name, layer, expert, bits)
 
 
 def oracle_experts(wl: mi.Workload, layer: int, bits: int | None = None):
-    bits = wl.bits if bits is None else bits
-    return lambda e: host_expert(wl.name, layer, int(e), bits)
+    return host_cache.experts_of(wl, layer, bits)
 
 
 def device_layers(wl, n_layers=None, bits=None, device="cuda"):

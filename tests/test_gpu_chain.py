@@ -1,12 +1,9 @@
-"""Chained decode: 48 layers with the residual stream and RMSNorm between
-layers, GPU against a free-running oracle on the same seeded inputs.
-
-The two sides differ by rounding (fp16 operands on the GPU), which can flip
-a routing decision only where two logits are nearly equal; the comparison
-walks the layers, requires identical routing and outputs within TOL, and
-accepts a routing difference only as a near-tie (oracle logit margin below
-NEAR_TIE), after which the streams are no longer comparable.  Batch
-invariance (4 tokens together vs each alone) is checked bitwise."""
+"""Chained decode through the layer-by-layer entry points: 48 layers of
+moe_route + moe_ffn_decode + moe_residual_rmsnorm with the residual stream
+and RMSNorm between layers, compared token by token and layer by layer with
+the oracle's free-running chain (chain_walk).  Batch invariance (4 tokens
+together vs each alone) is checked bitwise, and a HIP graph of the 48 layers
+replays bit-identically."""
 from __future__ import annotations
 
 import sys
@@ -15,14 +12,11 @@ import numpy as np
 import pytest
 
 import moe_inputs as mi
-import oracle.moe_oracle as O
-from helpers import TOL, device_layers, oracle_experts, row_rel_err
-import oracle_pool
+from chain_walk import full_depth_streams, stream_tokens, walk
+from helpers import device_layers
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
-
-NEAR_TIE = 2e-3
 
 
 def _say(msg):
@@ -52,54 +46,23 @@ class ChainRunner:
         self.ws_d = q.workspace(q.MOE_OP_DECODE, T, D, F, E, K)
 
     def run(self, x, record=False):
+        """Returns (ids, gates, h after each layer) stacked over the layers
+        when record is set."""
         q = self.q
         self.h.copy_(x)
-        recs = []
+        ids, gates, hs = [], [], []
         for l, (router, experts) in enumerate(self.layers):
             inp = self.h if l == 0 else self.u
-            if record:
-                u_l = inp.clone()
             q.moe_route(router, inp, self.ids, self.w, None, None, self.ws_r)
             q.moe_ffn_decode(experts, inp, self.ids, self.w, self.y, self.ws_d)
-            if record:
-                recs.append((u_l, self.ids.clone(), self.w.clone(), self.y.clone()))
             q.moe_residual_rmsnorm(self.h, self.y, self.u, 1e-6)
-        return recs
-
-
-def compare_free_running(wl, recs, x, bits, h_gpu):
-    """Walk the oracle chain alongside the recorded GPU layers."""
-    h = x.astype(np.float32)
-    matched = 0
-    for l, (u_g, ids_g, w_g, y_g) in enumerate(recs):
-        u = h if l == 0 else O.rmsnorm(h)
-        wh, bh = mi.router_host(wl, l)
-        ids_o, gates_o, z_o = O.route(u, wh, bh, wl.top_k)
-        ids_g = ids_g.cpu().numpy()
-        if not np.array_equal(ids_g, ids_o):
-            margins = []
-            for t in range(ids_o.shape[0]):
-                diff = np.nonzero(ids_g[t] != ids_o[t])[0]
-                if diff.size:
-                    j = diff[0]
-                    margins.append(z_o[t, ids_o[t, j]] - z_o[t, ids_g[t, j]])
-            print(f"layer {l}: routing differs at a near-tie, oracle margins {margins}")
-            assert max(margins) < NEAR_TIE, f"routing differs at layer {l} beyond a near-tie"
-            assert l >= 1
-            return matched
-        u_err = row_rel_err(u_g.cpu().numpy(), u)
-        assert u_err <= TOL, f"layer {l}: u differs by {u_err:.2e}"
-        assert np.max(np.abs(w_g.cpu().numpy() - gates_o)) <= TOL
-        oracle_pool.prefetch(wl.name, l, np.unique(ids_o), bits)
-        _, _, y_o = O.moe_layer(u, wh, bh, wl.top_k, oracle_experts(wl, l, bits), bits)
-        err = row_rel_err(y_g.cpu().numpy(), y_o)
-        assert err <= TOL, f"layer {l}: y differs by {err:.2e}"
-        h = (h + y_o).astype(np.float32)
-        matched += 1
-    err = row_rel_err(h_gpu, h)
-    print(f"all {matched} layers matched; final residual row_rel_err={err:.2e}")
-    assert err <= TOL
-    return matched
+            if record:
+                ids.append(self.ids.clone())
+                gates.append(self.w.clone())
+                hs.append(self.h.clone())
+        if not record:
+            return None
+        return (torch.stack(ids).cpu().numpy(), torch.stack(gates).cpu().numpy(), torch.stack(hs).cpu().numpy())
 
 
 def test_chain_decode_48_layers(q):
@@ -108,23 +71,27 @@ def test_chain_decode_48_layers(q):
     layers, ex, rt = device_layers(wl)
     x = mi.activations_host(wl)
     runner = ChainRunner(q, layers, 1)
-    recs = runner.run(torch.from_numpy(x).cuda(), record=True)
+    ids, gates, hl = runner.run(torch.from_numpy(x).cuda(), record=True)
     torch.cuda.synchronize()
     h_gpu = runner.h.cpu().numpy()
     # second run is bit-identical (deterministic kernels, self-resetting counters)
     runner.run(torch.from_numpy(x).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(runner.h.cpu().numpy(), h_gpu)
-    matched = compare_free_running(wl, recs, x, 2, h_gpu)
-    assert matched >= 8
+    walk(wl, 2, x, ids, gates, hl, h_gpu, label="layer calls, stream 0")
+    s = full_depth_streams(wl.name, 1)[0]
+    xs = stream_tokens(wl, [s])
+    o = runner.run(torch.from_numpy(xs).cuda(), record=True)
+    torch.cuda.synchronize()
+    walk(wl, 2, xs, *o, runner.h.cpu().numpy(), full=[0], label=f"layer calls, stream {s}")
     # the same 48 layers captured once in a graph and replayed
     g = torch.cuda.CUDAGraph()
     xd = torch.from_numpy(x).cuda()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
         runner.run(xd)          # warm-up on the capture stream
-    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
         runner.run(xd)
@@ -139,25 +106,24 @@ def test_chain_decode_48_layers(q):
 
 
 def test_chain_verify_4_tokens_3bit(q):
-    _say("48-layer verify chain, T=4, 3-bit experts; batch invariance vs 4 x T=1")
+    _say("48-layer verify chain, T=4, 3-bit experts; batch invariance vs 4 x T=1; full-depth tokens")
     wl = mi.WORKLOADS["verify4_3bit"]
     layers, ex, rt = device_layers(wl)
-    x = mi.activations_host(wl)
-    xd = torch.from_numpy(x).cuda()
+    xs = stream_tokens(wl, full_depth_streams(wl.name, 4))
+    xd = torch.from_numpy(xs).cuda()
     runner = ChainRunner(q, layers, 4)
-    recs = runner.run(xd, record=True)
+    ids, gates, hl = runner.run(xd, record=True)
     torch.cuda.synchronize()
     h_gpu = runner.h.cpu().numpy()
     one = ChainRunner(q, layers, 1)
     for t in range(4):
-        recs1 = one.run(xd[t:t + 1], record=True)
+        i1, g1, hl1 = one.run(xd[t:t + 1], record=True)
         torch.cuda.synchronize()
         assert np.array_equal(one.h.cpu().numpy()[0], h_gpu[t]), f"token {t}: T=4 differs from T=1"
-        for l in (0, 17, 47):
-            assert torch.equal(recs1[l][1][0], recs[l][1][t]) and torch.equal(recs1[l][3][0], recs[l][3][t])
-    uniq = [len(np.unique(r[1].cpu().numpy())) for r in recs]
+        assert np.array_equal(i1[:, 0], ids[:, t]) and np.array_equal(hl1[:, 0], hl[:, t])
+    uniq = [len(np.unique(ids[l])) for l in range(ids.shape[0])]
     print(f"distinct experts per layer: mean {np.mean(uniq):.1f} min {min(uniq)} max {max(uniq)}")
-    matched = compare_free_running(wl, recs, x, 3, h_gpu)
-    assert matched >= 8
+    matched, _ = walk(wl, 3, xs, ids, gates, hl, h_gpu, full=range(4), label="layer calls, 3-bit T=4")
+    assert matched == [48] * 4
     del layers, ex, rt
     torch.cuda.empty_cache()

@@ -1,6 +1,10 @@
-"""moe_decode_stack: a whole decode/verify step (every layer, one persistent
-launch) against the free-running CPU oracle, plus batch invariance,
-determinism across launches and the barrier error word."""
+"""moe_decode_stack: whole decode / verify steps (every layer in one
+persistent launch) against the oracle's free-running chain, token by token
+and layer by layer (chain_walk), plus batch invariance (a batch equals its
+tokens run alone, bitwise), determinism across launches and argument checks.
+
+Token streams that must match the oracle through all 48 layers are picked by
+the oracle alone (tests/golden/chain_margins.json)."""
 from __future__ import annotations
 
 import copy
@@ -12,13 +16,12 @@ import pytest
 
 import moe_inputs as mi
 import oracle.moe_oracle as O
+from chain_walk import full_depth_streams, stream_tokens, walk
 from helpers import TOL, device_stack, oracle_experts, row_rel_err
 import oracle_pool
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
-
-NEAR_TIE = 2e-3
 
 
 def _say(msg):
@@ -32,48 +35,55 @@ def q(need_gpu):
     return q
 
 
-def run_stack(q, st, x, T, record=True):
+def to_device(x: np.ndarray):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(x).cuda()
+
+
+def run_stack(q, st, x, ws=None):
+    """One moe_decode_stack launch; returns (h_out, ids, gates, h_layers) on
+    the host and the workspace."""
+    T = x.shape[0]
     L, K, D = st.n_layers, st.top_k, st.d_model
     h = torch.empty((T, D), device="cuda")
-    ids = torch.empty((L, T, K), dtype=torch.int32, device="cuda") if record else None
-    g = torch.empty((L, T, K), device="cuda") if record else None
-    ws = q.stack_workspace(st, T)
-    q.moe_decode_stack(st, x, h, ws, ids, g)
+    ids = torch.empty((L, T, K), dtype=torch.int32, device="cuda")
+    g = torch.empty((L, T, K), device="cuda")
+    hl = torch.empty((L, T, D), device="cuda")
+    ws = q.stack_workspace(st, T) if ws is None else ws
+    q.moe_decode_stack(st, x, h, ws, ids, g, h_layers=hl)
     torch.cuda.synchronize()
     err = int(ws[q.MOE_STACK_ERROR_OFFSET:q.MOE_STACK_ERROR_OFFSET + 4].view(torch.int32).item())
     assert err == 0, "grid barrier timed out"
-    return h, ids, g, ws
+    return h.cpu().numpy(), ids.cpu().numpy(), g.cpu().numpy(), hl.cpu().numpy(), ws
 
 
-def oracle_walk(wl, x, ids_g, gates_g, h_gpu, bits):
-    """Free-running oracle chain; returns layers matched.  A routing
-    difference is accepted only at a near-tie, after which the streams are no
-    longer comparable."""
-    h = O.as_f32_activations(x)
-    L = ids_g.shape[0]
-    for l in range(L):
-        u = h if l == 0 else O.rmsnorm(h)
-        wh, bh = mi.router_host(wl, l)
-        ids_o, gates_o, z_o = O.route(u, wh, bh if wl.zipf_bias else None, wl.top_k)
-        ig = ids_g[l]
-        if not np.array_equal(ig, ids_o):
-            margins = []
-            for t in range(ids_o.shape[0]):
-                diff = np.nonzero(ig[t] != ids_o[t])[0]
-                if diff.size:
-                    j = diff[0]
-                    margins.append(z_o[t, ids_o[t, j]] - z_o[t, ig[t, j]])
-            print(f"layer {l}: routing differs at a near-tie, oracle margins {margins}")
-            assert max(margins) < NEAR_TIE, f"routing differs at layer {l} beyond a near-tie"
-            return l
-        assert np.max(np.abs(gates_g[l] - gates_o)) <= TOL
-        oracle_pool.prefetch(wl.name, l, np.unique(ids_o), bits)
-        _, _, y_o = O.moe_layer(u, wh, bh if wl.zipf_bias else None, wl.top_k, oracle_experts(wl, l, bits), bits)
-        h = (h + y_o).astype(np.float32)
-    err = row_rel_err(h_gpu, h)
-    print(f"all {L} layers matched; final residual row_rel_err={err:.2e}")
-    assert err <= TOL
-    return L
+def check_batch_invariance(q, st, xd, out):
+    """Every token of a batch run equals the same token run alone, bitwise."""
+    h, ids, g, hl, _ = out
+    for t in range(xd.shape[0]):
+        h1, ids1, g1, hl1, _ = run_stack(q, st, xd[t:t + 1].contiguous())
+        assert np.array_equal(h1[0], h[t]), f"token {t}: batch result differs from the token alone"
+        assert np.array_equal(ids1[:, 0], ids[:, t]) and np.array_equal(g1[:, 0], g[:, t])
+        assert np.array_equal(hl1[:, 0], hl[:, t])
+
+
+@pytest.fixture(scope="module")
+def stack2(q):
+    wl = mi.WORKLOADS["decode_48layer"]
+    st, ex, rw, rb = device_stack(wl)
+    yield st
+    del st, ex, rw, rb
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def stack3(q, stack2):
+    wl = mi.WORKLOADS["verify4_3bit"]
+    st, ex, rw, rb = device_stack(wl)
+    yield st
+    del st, ex, rw, rb
+    torch.cuda.empty_cache()
 
 
 def test_stack_tiny_single_layer(q):
@@ -81,70 +91,88 @@ def test_stack_tiny_single_layer(q):
     wl = mi.WORKLOADS["tiny"]
     st, ex, rw, rb = device_stack(wl)
     x = mi.activations_host(wl)
-    h, ids, g, _ = run_stack(q, st, torch.from_numpy(x).cuda(), wl.n_tokens)
-    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
-    assert matched == 1
+    out = run_stack(q, st, torch.from_numpy(x).cuda())
+    matched, _ = walk(wl, 2, x, out[1], out[2], out[3], out[0], full=range(8), label="tiny")
+    assert matched == [1] * 8
 
 
-def test_stack_decode_48_layers(q):
-    _say("moe_decode_stack, 48 layers x 512 experts, T=1, 2-bit")
+def test_stack_decode_48_layers(q, stack2):
+    _say("moe_decode_stack, 48 layers x 512 experts, T=1, 2-bit: stream 0 and two full-depth streams")
     wl = mi.WORKLOADS["decode_48layer"]
-    st, ex, rw, rb = device_stack(wl)
+    st = stack2
     x = mi.activations_host(wl)
     xd = torch.from_numpy(x).cuda()
-    h, ids, g, ws = run_stack(q, st, xd, 1)
-    # the same workspace again (counters were reset by the kernel): identical bits
-    h2 = torch.empty_like(h)
-    q.moe_decode_stack(st, xd, h2, ws)
-    torch.cuda.synchronize()
-    assert torch.equal(h, h2)
-    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
-    assert matched >= 8
-    # a second token: stream 0 meets a genuine near-tie at layer 13
-    x1 = mi.activations_host(wl, 1, stream=1)
-    h1, ids1s, g1s, _ = run_stack(q, st, torch.from_numpy(x1).cuda(), 1)
-    matched1 = oracle_walk(wl, x1, ids1s.cpu().numpy(), g1s.cpu().numpy(), h1.cpu().numpy(), 2)
-    print(f"token stream 1: {matched1} layers matched")
-    assert matched1 >= 8
-    # the layer-by-layer entry points agree on routing for the first layer
-    router = q.Router(rw[0], rb[0], wl.top_k)
+    out = run_stack(q, st, xd)
+    # the same workspace again (the kernel resets its counters): identical bits
+    h2, _, _, _, _ = run_stack(q, st, xd, ws=out[4])
+    assert np.array_equal(out[0], h2)
+    walk(wl, 2, x, out[1], out[2], out[3], out[0], label="decode_48layer stream 0")
+    for s in full_depth_streams(wl.name, 2):
+        xs = stream_tokens(wl, [s])
+        o = run_stack(q, st, torch.from_numpy(xs).cuda())
+        walk(wl, 2, xs, o[1], o[2], o[3], o[0], full=[0], label=f"decode_48layer stream {s}")
+    # the layer-by-layer router agrees on the first layer
+    router = q.Router(st.router_w[0], st.router_b[0], wl.top_k)
     ids1 = torch.empty((1, wl.top_k), dtype=torch.int32, device="cuda")
     w1 = torch.empty((1, wl.top_k), device="cuda")
     q.moe_route(router, xd, ids1, w1, None, None, q.workspace(q.MOE_OP_ROUTE, 1, 2048, 768, 512, 10))
     torch.cuda.synchronize()
-    assert torch.equal(ids1[0], ids[0, 0])
-    del st, ex, rw, rb
-    torch.cuda.empty_cache()
+    assert np.array_equal(ids1.cpu().numpy()[0], out[1][0, 0])
 
 
-def test_stack_verify_4_tokens_3bit(q):
-    _say("moe_decode_stack, 48 layers, T=4, 3-bit; batch invariance vs T=1")
+def test_stack_verify_4_tokens_3bit(q, stack3):
+    _say("moe_decode_stack, 48 layers, T=4, 3-bit: the seeded batch, and a batch of 4 full-depth tokens")
     wl = mi.WORKLOADS["verify4_3bit"]
-    st, ex, rw, rb = device_stack(wl)
+    st = stack3
     x = mi.activations_host(wl)
     xd = torch.from_numpy(x).cuda()
-    h, ids, g, _ = run_stack(q, st, xd, 4)
-    for t in range(4):
-        h1, ids1, g1, _ = run_stack(q, st, xd[t:t + 1].contiguous(), 1)
-        assert torch.equal(h1[0], h[t]), f"token {t}: T=4 differs from T=1"
-        assert torch.equal(ids1[:, 0], ids[:, t]) and torch.equal(g1[:, 0], g[:, t])
-    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 3)
-    assert matched >= 8
-    del st, ex, rw, rb
-    torch.cuda.empty_cache()
+    out = run_stack(q, st, xd)
+    check_batch_invariance(q, st, xd, out)
+    walk(wl, 3, x, out[1], out[2], out[3], out[0], label="verify4_3bit seeded batch")
+    xs = stream_tokens(wl, full_depth_streams(wl.name, 4))
+    xsd = torch.from_numpy(xs).cuda()
+    o = run_stack(q, st, xsd)
+    check_batch_invariance(q, st, xsd, o)
+    matched, _ = walk(wl, 3, xs, o[1], o[2], o[3], o[0], full=range(4), label="verify4_3bit full-depth batch")
+    assert matched == [48] * 4
 
 
-def test_stack_batch_of_8(q):
-    _say("moe_decode_stack, 4 layers, T=8 (largest batch), 2-bit")
+@pytest.mark.parametrize("bits", [2, 3])
+def test_stack_verify_6_tokens(q, stack2, stack3, bits):
+    _say(f"moe_decode_stack, 48 layers, T=6 (1 + 5 drafts), {bits}-bit, full depth, vs 6 x T=1")
+    wl = mi.WORKLOADS["decode_48layer" if bits == 2 else "verify4_3bit"]
+    st = stack2 if bits == 2 else stack3
+    xs = stream_tokens(wl, full_depth_streams(wl.name, 6))
+    xd = torch.from_numpy(xs).cuda()
+    out = run_stack(q, st, xd)
+    check_batch_invariance(q, st, xd, out)
+    matched, _ = walk(wl, bits, xs, out[1], out[2], out[3], out[0], full=range(6), label=f"T=6 {bits}-bit")
+    assert matched == [48] * 6
+
+
+@pytest.mark.parametrize("T", [2, 8])
+def test_stack_3bit_batches(q, stack3, T):
+    _say(f"moe_decode_stack, 48 layers, 3-bit, T={T}: per-token oracle walk and batch invariance")
+    wl = mi.WORKLOADS["verify4_3bit"]
+    st = stack3
+    streams = full_depth_streams(wl.name, min(T, 6))
+    streams += [100 + i for i in range(T - len(streams))]          # seeded tokens with no margin guarantee
+    xs = stream_tokens(wl, streams)
+    xd = torch.from_numpy(xs).cuda()
+    out = run_stack(q, st, xd)
+    check_batch_invariance(q, st, xd, out)
+    walk(wl, 3, xs, out[1], out[2], out[3], out[0], full=range(min(T, 6)), label=f"3-bit T={T}")
+
+
+def test_stack_batch_of_8(q, stack2):
+    _say("moe_decode_stack, 48 layers, T=8 (largest batch), 2-bit")
     wl = mi.WORKLOADS["decode_48layer"]
-    st, ex, rw, rb = device_stack(wl, n_layers=4)
+    st = stack2
     x = mi.activations_host(wl, 8, stream=11)
     xd = torch.from_numpy(x).cuda()
-    h, ids, g, _ = run_stack(q, st, xd, 8)
-    h1, ids1, _, _ = run_stack(q, st, xd[5:6].contiguous(), 1)
-    assert torch.equal(h1[0], h[5])
-    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
-    assert matched >= 1
+    out = run_stack(q, st, xd)
+    check_batch_invariance(q, st, xd, out)
+    walk(wl, 2, x, out[1], out[2], out[3], out[0], label="2-bit T=8")
 
 
 def test_stack_single_layer_bf16_matches_layer_calls(q):
@@ -152,15 +180,9 @@ def test_stack_single_layer_bf16_matches_layer_calls(q):
     wl = mi.WORKLOADS["decode_1layer"]
     st, ex, rw, rb = device_stack(wl)
     x = mi.activations_host(wl)                       # bf16 bit patterns
-    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
-    h, ids, g, _ = run_stack(q, st, xd, 1)
-    # oracle: one layer, no norm before it: h = x + y
-    wh, bh = mi.router_host(wl, 0)
-    ids_o, gates_o, y_o = O.moe_layer(O.as_f32_activations(x), wh, bh, wl.top_k, oracle_experts(wl, 0, 2), 2)
-    assert np.array_equal(ids.cpu().numpy()[0], ids_o)
-    assert np.max(np.abs(g.cpu().numpy()[0] - gates_o)) <= TOL
-    want = (O.as_f32_activations(x) + y_o).astype(np.float32)
-    assert row_rel_err(h.cpu().numpy(), want) <= TOL
+    xd = to_device(x)
+    h, ids, g, hl, _ = run_stack(q, st, xd)
+    walk(wl, 2, x, ids, g, hl, h, full=[0], label="decode_1layer")
     # the layer-by-layer calls agree on routing, and on the layer output to rounding
     router = q.Router(rw[0], rb[0], wl.top_k)
     experts = q.Experts(ex["gate_q"][0], ex["up_q"][0], ex["down_q"][0], ex["gate_s"][0], ex["up_s"][0],
@@ -171,26 +193,24 @@ def test_stack_single_layer_bf16_matches_layer_calls(q):
     y1 = torch.empty((1, 2048), device="cuda")
     q.moe_ffn_decode(experts, xd, ids1, w1, y1, q.workspace(q.MOE_OP_DECODE, 1, 2048, 768, 512, 10))
     torch.cuda.synchronize()
-    assert torch.equal(ids1[0], ids[0, 0])
-    assert torch.max(torch.abs(w1[0] - g[0, 0])).item() <= 1e-6
+    assert np.array_equal(ids1.cpu().numpy()[0], ids[0, 0])
+    assert np.max(np.abs(w1.cpu().numpy()[0] - g[0, 0])) <= 1e-6
     h_layers = (xd.float() + y1).cpu().numpy()
-    assert row_rel_err(h.cpu().numpy(), h_layers) <= TOL
+    assert row_rel_err(h, h_layers) <= TOL
     del st, ex, rw, rb
     torch.cuda.empty_cache()
 
 
-def test_stack_256_experts_two_tokens(q):
-    _say("moe_decode_stack, 4 layers x 256 experts (one router expert per workgroup), T=2, batch invariance")
+def test_stack_256_experts(q):
+    _say("moe_decode_stack, 4 layers x 256 experts (one router expert per workgroup), T=2 and T=6")
     wl = mi.WORKLOADS["coder_256"]
     st, ex, rw, rb = device_stack(wl)
-    x = mi.activations_host(wl)
-    xd = torch.from_numpy(x).cuda()
-    h, ids, g, _ = run_stack(q, st, xd, 2)
-    for t in range(2):
-        h1, ids1, g1, _ = run_stack(q, st, xd[t:t + 1].contiguous(), 1)
-        assert torch.equal(h1[0], h[t]) and torch.equal(ids1[:, 0], ids[:, t]) and torch.equal(g1[:, 0], g[:, t])
-    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
-    assert matched >= 1
+    for T, stream in ((2, 0), (6, 1)):
+        x = mi.activations_host(wl, T, stream=stream)
+        xd = torch.from_numpy(x).cuda()
+        out = run_stack(q, st, xd)
+        check_batch_invariance(q, st, xd, out)
+        walk(wl, 2, x, out[1], out[2], out[3], out[0], label=f"256 experts T={T}")
     del st, ex, rw, rb
     torch.cuda.empty_cache()
 
@@ -201,12 +221,9 @@ def test_stack_batch_of_3(q):
     st, ex, rw, rb = device_stack(wl, n_layers=4)
     x = mi.activations_host(wl, 3, stream=7)
     xd = torch.from_numpy(x).cuda()
-    h, ids, g, _ = run_stack(q, st, xd, 3)
-    for t in range(3):
-        h1, ids1, g1, _ = run_stack(q, st, xd[t:t + 1].contiguous(), 1)
-        assert torch.equal(h1[0], h[t]) and torch.equal(ids1[:, 0], ids[:, t]) and torch.equal(g1[:, 0], g[:, t])
-    matched = oracle_walk(wl, x, ids.cpu().numpy(), g.cpu().numpy(), h.cpu().numpy(), 2)
-    assert matched >= 1
+    out = run_stack(q, st, xd)
+    check_batch_invariance(q, st, xd, out)
+    walk(wl, 2, x, out[1], out[2], out[3], out[0], label="T=3, 4 layers")
     del st, ex, rw, rb
     torch.cuda.empty_cache()
 
@@ -222,7 +239,7 @@ def test_stack_abi_errors(q):
 
     def call(stack, xx, n, hh, w, nbytes, ids=None, gates=None):
         return lib.moe_decode_stack(ctypes.byref(stack._c), q._ptr(xx), q._dtype(xx), n, 1e-6, q._ptr(hh),
-                                    q._ptr(ids), q._ptr(gates), q._ptr(w), nbytes, None)
+                                    q._ptr(ids), q._ptr(gates), None, q._ptr(w), nbytes, None)
 
     assert call(st, x, 8, h, ws, ws.numel()) == q.MOE_OK
     torch.cuda.synchronize()

@@ -300,9 +300,35 @@ def pin_chain(O):
     h1, recs = O.moe_chain(x, 1, lambda l: (wr[l], None), lambda l: (lambda i: exps[i]), 2, 2)
     _, _, y = O.moe_layer(x, wr[0], None, 2, lambda i: exps[i], 2)
     assert np.array_equal(h1, x + y)
+    # two layers: the second layer reads the normalised residual and its
+    # output is added to the residual (not to its own input)
     h2, recs = O.moe_chain(x, 2, lambda l: (wr[l], None), lambda l: (lambda i: exps[i]), 2, 2)
-    u1 = recs[1][0].astype(np.float64)
-    assert np.allclose(np.mean(u1 * u1, axis=1), 1.0, rtol=1e-4)
+    u1 = O.rmsnorm(h1)
+    _, _, y1 = O.moe_layer(u1, wr[1], None, 2, lambda i: exps[i], 2)
+    assert np.array_equal(recs[0][4], h1) and np.array_equal(recs[1][0], u1)
+    assert np.array_equal(h2, (h1 + y1).astype(np.float32)) and np.array_equal(recs[1][4], h2)
+    m = np.mean(recs[1][0].astype(np.float64) ** 2, axis=1)
+    assert np.allclose(m, 1.0, rtol=1e-4)
+
+
+def pin_chain_hand(O):
+    """Two layers of the hand-built expert (E = 1, k = 1, gate 1) on a one-hot
+    token, evaluated in closed form with Python floats: layer 1 sees the
+    RMS-normalised residual h1 = x + y0, and h2 = h1 + y1."""
+    stored, y0 = _hand_expert()
+    lg = np.array([1, -1, -2, 0] * 8) * 0.5
+    lu = np.array([-2, 1, 1, -1, 0, 1, -2, 1] * 4) * 0.25
+    d_lev = (np.arange(32)[:, None] * 7 + np.arange(32)[None, :] * 3) % 4 - 2
+    x = np.zeros((1, 32), np.float32)
+    x[0, 3] = 1.0
+    h1 = [float(x[0, i]) + float(y0[i]) for i in range(32)]
+    rms = math.sqrt(sum(v * v for v in h1) / 32 + 1e-6)
+    a = h1[3] / rms                                  # the only input the gate/up rows read
+    h = [(a * lg[j]) / (1 + math.exp(-(a * lg[j]))) * (a * lu[j]) for j in range(32)]
+    h2 = [h1[i] + sum(h[j] * d_lev[i, j] for j in range(32)) for i in range(32)]
+    got, recs = O.moe_chain(x, 2, lambda l: (np.zeros((32, 1), np.float32), None), lambda l: (lambda e: stored), 1, 2)
+    assert np.allclose(recs[0][4][0], h1, rtol=1e-6, atol=1e-6)
+    assert np.allclose(got[0], h2, rtol=1e-5, atol=1e-5 * max(abs(v) for v in h2))
 
 
 def pin_token_independence(O):
@@ -321,7 +347,7 @@ def pin_token_independence(O):
 PINS = [pin_golden_blocks, pin_pack_unpack_bijection, pin_quantize_roundtrip, pin_quantize_error_bound,
         pin_logits_exact, pin_logits_bf16_input, pin_topk_bruteforce, pin_topk_ties_and_zero,
         pin_gate_invariants, pin_buckets, pin_expert_hand, pin_dense_fp64, pin_combine_and_slots,
-        pin_rmsnorm, pin_chain, pin_token_independence]
+        pin_rmsnorm, pin_chain, pin_chain_hand, pin_token_independence]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -413,7 +439,35 @@ def _mut_combine_slot_shift(orig):
     return "combine", lambda g, o: orig(np.roll(g, 1, axis=1), o)
 
 
-MUTATIONS = [_mut_unpack2_reversed, _mut_unpack3_straddle, _mut_dequant_offset, _mut_logits_no_bias,
+def _chain_variant(update, norm_first=False, norm_rest=True):
+    """A moe_chain built from the oracle's own layer and norm but composed
+    wrongly: ``update(h, u, y)`` forms the next residual."""
+    def chain(x, n_layers, router_of, experts_of, k, bits, eps=1e-6, prepare_of=None):
+        h = O.as_f32_activations(x)
+        recs = []
+        for l in range(n_layers):
+            u = O.rmsnorm(h, eps) if (norm_first if l == 0 else norm_rest) else h
+            w, b = router_of(l)
+            ids, gates, y = O.moe_layer(u, w, b, k, experts_of(l), bits)
+            h = update(h, u, y).astype(np.float32)
+            recs.append((u, ids, gates, y, h))
+        return h, recs
+    return chain
+
+
+def _mut_chain_residual_on_u(orig):
+    return "moe_chain", _chain_variant(lambda h, u, y: u + y)
+
+
+def _mut_chain_norm_first_layer(orig):
+    return "moe_chain", _chain_variant(lambda h, u, y: h + y, norm_first=True)
+
+
+def _mut_chain_no_norm(orig):
+    return "moe_chain", _chain_variant(lambda h, u, y: h + y, norm_rest=False)
+
+
+MUTATIONS = [_mut_chain_residual_on_u, _mut_chain_norm_first_layer, _mut_chain_no_norm, _mut_unpack2_reversed, _mut_unpack3_straddle, _mut_dequant_offset, _mut_logits_no_bias,
              _mut_logits_fp32, _mut_topk_high_id, _mut_gates_all_experts, _mut_buckets_descending,
              _mut_swiglu_swapped, _mut_combine_unweighted, _mut_rmsnorm_no_eps, _mut_combine_slot_shift]
 
