@@ -184,6 +184,17 @@ int moe_ffn_decode(const moe_experts_t* experts, const void* x, int x_dtype, int
                    const int32_t* topk_ids, const float* topk_w, int top_k, float* y,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* moe_ffn_decode without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  Same arguments (minus ws), limits and
+ * results (bitwise) as moe_ffn_decode; the SwiGLU intermediate lives in a
+ * library-owned 8 MiB array of device memory per device, held until the
+ * process ends, and nothing is allocated or freed.  Every call on a device
+ * shares that array, so calls that overlap on one device (different streams
+ * or threads) race and give undefined results; serialise them. */
+int moe_ffn_decode_noalloc(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens,
+                           const int32_t* topk_ids, const float* topk_w, int top_k, float* y, void* stream);
+
 /* Expert FFN and combine for a prefill chunk, as grouped GEMMs over the
  * expert buckets produced by moe_route.  Same result as moe_ffn_decode
  * (within fp16-operand rounding: activations and the SwiGLU intermediate

@@ -21,7 +21,7 @@ __all__ = [
     "stack_workspace", "moe_prefill_stack_workspace_size", "prefill_stack_workspace", "moe_prefill_stack",
     "MOE_STACK_ERROR_OFFSET", "MoeError", "Router", "Experts", "Stack", "lib_path", "library",
     "moe_workspace_size", "workspace", "moe_route", "moe_ffn_decode", "moe_ffn_prefill", "moe_decode_stack",
-    "moe_residual_rmsnorm", "moe_status_string", "EXPORTED_SYMBOLS",
+    "moe_residual_rmsnorm", "moe_status_string", "EXPORTED_SYMBOLS", "moe_ffn_decode_noalloc",
 ]
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_DEVICE, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5
@@ -29,8 +29,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
 MOE_STACK_ERROR_OFFSET = 2304
 
-EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_ffn_decode", "moe_ffn_prefill",
-                    "moe_stack_workspace_size", "moe_decode_stack", "moe_prefill_stack_workspace_size",
+EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_ffn_decode", "moe_ffn_decode_noalloc",
+                    "moe_ffn_prefill", "moe_stack_workspace_size", "moe_decode_stack", "moe_prefill_stack_workspace_size",
                     "moe_prefill_stack", "moe_residual_rmsnorm", "moe_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_route.restype = I
     lib.moe_ffn_decode.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, P, I, P, P, Z, P]
     lib.moe_ffn_decode.restype = I
+    lib.moe_ffn_decode_noalloc.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, P, I, P, P]
+    lib.moe_ffn_decode_noalloc.restype = I
     lib.moe_ffn_prefill.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, I, P, P, P, P, Z, P]
     lib.moe_ffn_prefill.restype = I
     lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_StackT), I]
@@ -248,6 +250,15 @@ def moe_ffn_decode(experts: Experts, x: torch.Tensor, topk_ids: torch.Tensor, to
                                 _ptr(topk_w), topk_ids.shape[1], _ptr(y), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(stream))
     _check("moe_ffn_decode", st)
+
+
+def moe_ffn_decode_noalloc(experts: Experts, x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                           y: torch.Tensor, stream=None) -> None:
+    """moe_ffn_decode with the library's per-device scratch instead of a
+    workspace (no allocation; overlapping calls on one device race)."""
+    st = library.moe_ffn_decode_noalloc(ctypes.byref(experts._c), _ptr(x), _dtype(x), x.shape[0], _ptr(topk_ids),
+                                        _ptr(topk_w), topk_ids.shape[1], _ptr(y), _stream(stream))
+    _check("moe_ffn_decode_noalloc", st)
 
 
 def moe_ffn_prefill(experts: Experts, x: torch.Tensor, topk_w: torch.Tensor, bucket_offsets: torch.Tensor,

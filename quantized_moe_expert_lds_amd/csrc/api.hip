@@ -146,6 +146,28 @@ int moe_ffn_decode(const moe_experts_t* experts, const void* x, int x_dtype, int
                                     (hipStream_t)stream));
 }
 
+int moe_ffn_decode_noalloc(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens,
+                           const int32_t* topk_ids, const float* topk_w, int top_k, float* y, void* stream) {
+    int st = check_experts(experts);
+    if (st) return st;
+    if (!x || !topk_ids || !topk_w || !y || n_tokens <= 0 || top_k <= 0) return MOE_ERR_ARG;
+    const int xf = dtype_flag(x_dtype);
+    if (xf < 0) return MOE_ERR_ARG;
+    if (n_tokens > kMaxDecodeTokens || top_k > kMaxTopK || top_k > experts->n_experts)
+        return MOE_ERR_UNSUPPORTED;
+    if (!decode_supported(n_tokens, top_k, experts->d_ff)) return MOE_ERR_UNSUPPORTED;
+    const DecodeWs L = decode_ws_layout(n_tokens, experts->d_ff, top_k);
+    if (L.total > kDecodeScratchBytes) return MOE_ERR_UNSUPPORTED;
+    if ((st = check_device())) return st;
+    char* scratch = nullptr;
+    if (decode_noalloc_scratch(&scratch) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    return hip_status(launch_decode(*experts, x, xf, n_tokens, topk_ids, topk_w, top_k, y, scratch, L,
+                                    (hipStream_t)stream));
+}
+
 int moe_ffn_prefill(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens, const float* topk_w,
                     int top_k, const int32_t* bucket_offsets, const int32_t* bucket_pairs, float* y, void* ws,
                     size_t ws_bytes, void* stream) {

@@ -77,6 +77,13 @@ inline DecodeWs decode_ws_layout(int T, int F, int K) {
     return w;
 }
 
+// moe_ffn_decode_noalloc: the per-device scratch that replaces the decode
+// workspace (8 MiB: the SwiGLU intermediate of 8 tokens x 64 slots x 4096
+// d_ff values, kept as two fp16 halves each) and its device address on the
+// current device.
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+hipError_t decode_noalloc_scratch(char** ptr);
+
 inline int prefill_max_tiles(int T, int E, int K) {
     const long long P = (long long)T * K;
     const long long nonempty = P < E ? P : E;

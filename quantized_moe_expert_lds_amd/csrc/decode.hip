@@ -22,6 +22,8 @@
 //
 // Every per-token quantity is computed by the same instruction sequence for
 // any batch size, so results do not depend on n_tokens (bitwise).
+#include <atomic>
+
 #include "common.hpp"
 
 namespace {
@@ -336,9 +338,41 @@ namespace qmoe {
 bool decode_supported(int T, int K, int F) { return down_rows(T, K, F) > 0; }
 }  // namespace qmoe
 
+// ------------------------------------------------ allocation-free variant
+// moe_ffn_decode_noalloc keeps the SwiGLU intermediate in this file-scope
+// array instead of a caller workspace.  Each device holds its own copy until
+// the process ends.  On the host, `scratch` names only a stand-in for the
+// symbol: host code passes kernels the device address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
 namespace {
 
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[qmoe::kDecodeScratchBytes];
+std::atomic<char*> g_scratch_ptr[kScratchDevices];
+
 }  // namespace
+
+namespace qmoe {
+
+hipError_t decode_noalloc_scratch(char** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        p = static_cast<char*>(a);
+        // two threads racing here store the same address
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
+}  // namespace qmoe
 
 namespace qmoe {
 
