@@ -228,25 +228,32 @@ size_t moe_stack_workspace_size(const moe_stack_t* model, int n_tokens);
  *   h_out = h_L
  * Routing follows moe_route (fp64 logits, ties to the lower id; the logits
  * are summed in a different order than in moe_route, so a logit can differ
- * in its last bits) and the expert math follows moe_ffn_decode.  Results
- * for a token do not depend on n_tokens (bitwise).
+ * in its last bits) and the expert math follows moe_ffn_decode (u and the
+ * SwiGLU intermediate enter the fp16 dot products as two fp16 halves each,
+ * ~22 significant bits, with fp32 accumulation).  Results for a token do not
+ * depend on n_tokens or on the other tokens (bitwise).
  *
  * Runs as one cooperative launch with one workgroup per compute unit that
- * stays resident for all layers; layers are separated by grid barriers
- * instead of kernel boundaries.  If the workgroups cannot all be resident
- * the launch fails with MOE_ERR_HIP; should a barrier nevertheless wait
- * longer than a few seconds, the kernel stops, the int at byte offset
+ * stays resident for all layers; the workgroups hand logits, residual rows
+ * and SwiGLU rows to each other through the workspace, tagged with per-token-
+ * slot epochs kept in its header (a workspace can serve any sequence of
+ * launches and batch sizes).  If the workgroups cannot all be resident the
+ * launch fails with MOE_ERR_HIP; should a wait nevertheless last longer than
+ * a few seconds, the kernel stops, the int at byte offset
  * MOE_STACK_ERROR_OFFSET of ws becomes nonzero, the outputs are undefined and
  * ws must be zero-filled again before reuse.
  *
- *   x            device [n_tokens][d_model], fp32 or bf16
+ *   x            device [n_tokens][d_model], fp32 or bf16 (|x| < 65504)
  *   h_out        device fp32 [n_tokens][d_model] (output)
  *   topk_ids_out device int32 [L][n_tokens][top_k] or NULL (output)
  *   topk_w_out   device fp32  [L][n_tokens][top_k] or NULL (output; both or neither)
  *   h_layers_out device fp32  [L][n_tokens][d_model] or NULL (output): h_{l+1}
  *                after every layer l (its last row block equals h_out)
- * Supported: 1 <= n_tokens <= 8, d_model and d_ff multiples of 32 and
- * <= 4096, n_experts <= min(1024, 4 x compute units), top_k <= min(n_experts, 64). */
+ *   ws           device, moe_stack_workspace_size(model, n_tokens) bytes,
+ *                256-byte aligned, zero-filled before its first use
+ * Supported: 1 <= n_tokens <= 8, d_model and d_ff multiples of 32,
+ * d_model <= 2048, d_ff <= 4096, n_experts <= min(1024, 4 x compute units),
+ * top_k <= min(n_experts, 64). */
 int moe_decode_stack(const moe_stack_t* model, const void* x, int x_dtype, int n_tokens, double eps,
                      float* h_out, int32_t* topk_ids_out, float* topk_w_out, float* h_layers_out, void* ws,
                      size_t ws_bytes, void* stream);

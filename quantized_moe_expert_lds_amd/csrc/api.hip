@@ -217,7 +217,7 @@ int moe_decode_stack(const moe_stack_t* m, const void* x, int x_dtype, int n_tok
     const StackWs Lw = stack_ws_layout(n_tokens, D, F, E, K, G, L);
     if ((st = check_ws(ws, ws_bytes, Lw.total))) return st;
     // router experts and d_model rows per workgroup
-    if ((E + G - 1) / G > 4 || (D + G - 1) / G > 32) return MOE_ERR_UNSUPPORTED;
+    if ((E + G - 1) / G > 4 || (D + G - 1) / G > 16) return MOE_ERR_UNSUPPORTED;
     if (stack_lds_bytes(n_tokens, D, F, E, K, G, m->bits) > kStackLdsLimit)
         return MOE_ERR_UNSUPPORTED;
     return hip_status(launch_decode_stack(*m, x, xf, n_tokens, h_out, ids_out, gates_out, h_layers_out, eps,

@@ -41,7 +41,7 @@ struct StackWs {
     size_t sync, zbuf, hres, ssp, hbuf, total;
 };
 constexpr int kStackMaxGrid = 1024;      // workspace sized for up to this many workgroups
-constexpr int kStackMaxD = 4096;
+constexpr int kStackMaxD = 2048;
 constexpr size_t kStackLdsLimit = 160 * 1024;
 StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L);
 size_t stack_lds_bytes(int T, int D, int F, int E, int K, int G, int bits);
@@ -70,10 +70,11 @@ struct PrefillStackWs {
     PrefillWs pl;
 };
 
+// the SwiGLU intermediate as two fp16 halves (hi, then lo) per value
 inline DecodeWs decode_ws_layout(int T, int F, int K) {
     DecodeWs w{};
     w.h = 0;
-    w.total = align256(sizeof(uint16_t) * (size_t)T * K * F);
+    w.total = align256(2 * sizeof(uint16_t) * (size_t)T * K * F);
     return w;
 }
 
@@ -148,8 +149,8 @@ hipError_t launch_prefill(const moe_experts_t& ex, const void* x, int x_bf16, in
                           int K, const int32_t* offsets, const int32_t* pairs, float* y, char* ws,
                           const PrefillWs& L, hipStream_t s);
 hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, int T, float* h_out,
-                               int32_t* ids_out, float* gates_out, float* h_layers, double eps, char* ws, const StackWs& L, int G,
-                               hipStream_t s);
+                               int32_t* ids_out, float* gates_out, float* h_layers, double eps, char* ws,
+                               const StackWs& L, int G, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float* h, const float* y, float* u, int T, int d, double eps,
                                    hipStream_t s);
 hipError_t launch_to_f32(const void* x, int x_bf16, size_t n, float* out, hipStream_t s);

@@ -41,7 +41,9 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
 }
 
 // x values of block kb of token row xrow -> 16 fp16 pairs in the unpack
-// order: pair m = (x[m], x[m+8]), pair 8+m = (x[16+m], x[24+m]).
+// order (pair m = (x[m], x[m+8]), pair 8+m = (x[16+m], x[24+m])), as two
+// halves: xp[0..15] = fp16(x), xp[16..31] = fp16(x - fp16(x)).  Together
+// they carry ~22 significant bits of x into the dot products.
 __device__ __forceinline__ void load_x_pairs(const void* x, int x_bf16, size_t row_off, int kb,
                                              uint32_t* xp) {
     float v[32];
@@ -70,10 +72,17 @@ __device__ __forceinline__ void load_x_pairs(const void* x, int x_bf16, size_t r
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        half2_t a = {(_Float16)v[m], (_Float16)v[m + 8]};
-        half2_t b = {(_Float16)v[16 + m], (_Float16)v[24 + m]};
-        xp[m] = as_u32(a);
-        xp[8 + m] = as_u32(b);
+        const int ia[4] = {m, m + 8, 16 + m, 24 + m};
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hi[i] = (_Float16)v[ia[i]];
+            lo[i] = (_Float16)(v[ia[i]] - (float)hi[i]);
+        }
+        xp[m] = as_u32(half2_t{hi[0], hi[1]});
+        xp[8 + m] = as_u32(half2_t{hi[2], hi[3]});
+        xp[16 + m] = as_u32(half2_t{lo[0], lo[1]});
+        xp[24 + m] = as_u32(half2_t{lo[2], lo[3]});
     }
 }
 
@@ -97,16 +106,21 @@ __device__ __forceinline__ void block_levels(const uint32_t* w, uint32_t* lv) {
     }
 }
 
-__device__ __forceinline__ float dot16(const uint32_t* lv, const uint32_t* xp) {
+// levels . (hi + lo) with the operand halves as load_x_pairs lays them out;
+// the small lo terms are summed first
+__device__ __forceinline__ float dot32(const uint32_t* lv, const uint32_t* xp) {
     float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_fdot2(as_half2(lv[m]), as_half2(xp[16 + m]), acc, false);
 #pragma unroll
     for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_fdot2(as_half2(lv[m]), as_half2(xp[m]), acc, false);
     return acc;
 }
 
 // ------------------------------------------------------------- gate / up
-// grid (T*K, F/16), block 256.  hbuf: fp16 [T*K][F], each 32-block stored in
-// the unpack pair order (position perm32(i) holds element i).
+// grid (T*K, F/16), block 256.  hbuf: fp16 [2][T*K][F]: hbuf[0] holds
+// fp16(h), hbuf[1] fp16(h - fp16(h)), each 32-block stored in the unpack pair
+// order (position perm32(i) holds element i).
 template <int T, int BITS>
 __global__ __launch_bounds__(256) void decode_gateup_kernel(moe_experts_t ex, const void* __restrict__ x,
                                                             int x_bf16, const int32_t* __restrict__ ids,
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(moe_experts_t ex, co
             }
             sc[r] = half_bits_to_f32(srow[r][kb]);
         }
-        uint32_t xp[T][16];
+        uint32_t xp[T][32];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             if (s_pair[t] >= 0) load_x_pairs(x, x_bf16, (size_t)t * D, kb, xp[t]);
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(moe_experts_t ex, co
             block_levels<BITS>(q[r], lv);
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                if (s_pair[t] >= 0) acc[r][t] = fmaf(sc[r], dot16(lv, xp[t]), acc[r][t]);
+                if (s_pair[t] >= 0) acc[r][t] = fmaf(sc[r], dot32(lv, xp[t]), acc[r][t]);
         }
     }
     // wavefront sums (same butterfly for every row and token)
@@ -203,7 +217,10 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(moe_experts_t ex, co
                 const float h = silu_mul(acc[r][t], acc[kGuRowsPerWave + r][t]);
                 const int f = f0 + r;
                 const _Float16 hh = (_Float16)h;
-                hbuf[(size_t)s_pair[t] * F + (f & ~31) + perm32(f & 31)] = __builtin_bit_cast(uint16_t, hh);
+                const _Float16 hl = (_Float16)(h - (float)hh);
+                const size_t hi = (size_t)s_pair[t] * F + (f & ~31) + perm32(f & 31);
+                hbuf[hi] = __builtin_bit_cast(uint16_t, hh);
+                hbuf[(size_t)T * K * F + hi] = __builtin_bit_cast(uint16_t, hl);
             }
         }
 }
@@ -271,21 +288,24 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe_experts_t ex, cons
         for (int t = 0; t < T; ++t) {
             const int pr = s_pair[p * T + t];
             if (pr < 0) continue;
-            uint32_t hp[16];
-            const uint4* hs = reinterpret_cast<const uint4*>(hbuf + (size_t)pr * F + 32 * kb);
+            uint32_t hp[32];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 u = hs[v];
-                hp[4 * v] = u.x;
-                hp[4 * v + 1] = u.y;
-                hp[4 * v + 2] = u.z;
-                hp[4 * v + 3] = u.w;
+            for (int half = 0; half < 2; ++half) {
+                const uint4* hs = reinterpret_cast<const uint4*>(hbuf + (size_t)half * P * F + (size_t)pr * F + 32 * kb);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 u = hs[v];
+                    hp[16 * half + 4 * v] = u.x;
+                    hp[16 * half + 4 * v + 1] = u.y;
+                    hp[16 * half + 4 * v + 2] = u.z;
+                    hp[16 * half + 4 * v + 3] = u.w;
+                }
             }
 #pragma unroll
             for (int r = 0; r < kDownRows; ++r) {
                 uint32_t lv[16];
                 block_levels<BITS>(q[r], lv);
-                part[((size_t)pr * kDownRows + r) * nkb + kb] = sc[r] * dot16(lv, hp);
+                part[((size_t)pr * kDownRows + r) * nkb + kb] = sc[r] * dot32(lv, hp);
             }
         }
     }

@@ -6,22 +6,27 @@ using namespace qmoe::stk;
 
 namespace qmoe {
 
+// Workspace: header, then the tagged residual-row, logit and flag buffers
+// (sized for kStackMaxGrid workgroups and kSlots token slots, so their
+// layout is the same for every batch size and device), then the per-layer
+// SwiGLU rows.
 StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L) {
     StackWs w{};
     size_t off = 0;
     w.sync = off;
-    off += align256(sizeof(int) * 10 * kLine);
-    w.zbuf = off;
-    off += align256(sizeof(double) * (size_t)L * G * T * kZW);
-    w.hres = off;
-    off += align256(sizeof(float) * (size_t)L * G * T * kHW);
-    w.ssp = off;
-    off += align256(sizeof(double) * (size_t)L * G * 16);
+    off += kHdrBytes;
+    w.zbuf = off;                                              // residual rows + sums of squares
+    off += align256(sizeof(u64) * (size_t)kStackMaxGrid * kSlots * kSLW);
+    w.hres = off;                                              // logits
+    off += align256(sizeof(u64) * (size_t)kStackMaxGrid * kSlots * kLGW);
+    w.ssp = off;                                               // flags
+    off += align256(sizeof(u64) * (size_t)kStackMaxGrid * kFLW);
     w.hbuf = off;
     off += align256(sizeof(uint32_t) * (size_t)L * T * K * (F / 16) * kHBW);
     w.total = off;
     (void)D;
     (void)E;
+    (void)G;
     return w;
 }
 
@@ -93,10 +98,10 @@ hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, 
     P.h_layers = h_layers;
     P.eps = eps;
     P.G = G;
-    P.sync = (int*)(ws + L.sync);
-    P.zb = (double*)(ws + L.zbuf);
-    P.hb = (float*)(ws + L.hres);
-    P.sb = (double*)(ws + L.ssp);
+    P.hdr = (uint32_t*)(ws + L.sync);
+    P.sl = (u64*)(ws + L.zbuf);
+    P.lg = (u64*)(ws + L.hres);
+    P.fl = (u64*)(ws + L.ssp);
     P.hp = (uint32_t*)(ws + L.hbuf);
     const StackLds pl = stack_lds_plan(T, m.d_model, m.d_ff, m.n_experts, m.top_k, G, m.bits);
     P.lds_us = (int)pl.us;

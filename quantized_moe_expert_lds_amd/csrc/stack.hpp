@@ -1,6 +1,7 @@
 // Declarations shared by the persistent decode-step kernel (stack_kernel.hpp,
 // instantiated per batch size in stack_t1.hip .. stack_t8.hip) and its host
-// side (stack.hip): kernel parameters, constants and the LDS sub-layout.
+// side (stack.hip): kernel parameters, constants and the layouts of the
+// workspace and of LDS.
 #pragma once
 
 #include "common.hpp"
@@ -8,16 +9,26 @@
 namespace qmoe {
 namespace stk {
 
+typedef unsigned long long u64;
 
 constexpr int kThreads = 256;
+constexpr int kSlots = 8;              // token slots of the tagged buffers (their layout never depends on T)
 constexpr int kMaxEPW = 4;             // router experts per workgroup
-constexpr int kLine = 64;              // ints between barrier counters (256 B)
 constexpr long long kTimeoutTicks = 400000000LL;   // 4 s of the 100 MHz wall clock
-constexpr int kZW = 16;                // doubles per (workgroup, token) logit line
-constexpr int kHW = 32;                // floats per (workgroup, token) residual line
-constexpr int kHBW = 32;               // words per (pair, 16-row chunk) h line
+constexpr int kSLW = 32;               // tagged words per (workgroup, token) residual line
+constexpr int kSSWord = 16;            // word of that line holding the sum of squares (2 words)
+constexpr int kLGW = 8;                // tagged words per (workgroup, token) logit line
+constexpr int kFLW = 8;                // words per workgroup flag (64 B apart)
+constexpr int kHBW = 32;               // words per (pair, 16-row chunk) h line (8 hi pairs, 8 lo pairs)
 constexpr int kMaxItemsInFlight = 2;   // gate/up items whose loads are issued together
-constexpr int kXhWords = 17;           // words per fp16 u block row in LDS (16 pairs + 1 pad)
+constexpr int kXhWords = 36;           // words per u block row in LDS: 16 hi pairs, 16 lo pairs, 4 pad
+constexpr int kMaxDPW = 16;            // d_model rows per workgroup
+// workspace header (uint32 words): epoch bases of the 8 token slots, the
+// launch-completion counter and the error word
+constexpr int kHdrBase = 0;
+constexpr int kHdrDone = 64;
+constexpr int kHdrErr = MOE_STACK_ERROR_OFFSET / 4;
+constexpr size_t kHdrBytes = 4096;
 
 struct StackParams {
     moe_stack_t m;
@@ -30,11 +41,11 @@ struct StackParams {
     float* h_layers;    // [L][T][D] residual after each layer, or null
     double eps;
     int G;
-    int* sync;          // 8 counters (256 B apart), done counter, error flag
-    double* zb;         // [L][G][T][kZW]      logits of the workgroup's experts
-    float* hb;          // [L][G][T][kHW]      residual rows of the workgroup
-    double* sb;         // [L][G][16]          sums of squares per token
-    uint32_t* hp;       // [L][T*K][F/16][kHBW] SwiGLU h, fp16 pairs in unpack order
+    uint32_t* hdr;      // workspace header (see kHdr*)
+    u64* sl;            // [G][T][kSLW]  residual rows of workgroup g (+ sum of squares), tagged
+    u64* lg;            // [G][T][kLGW]  fp64 logits of workgroup g's experts (lo, hi words), tagged
+    u64* fl;            // [G][kFLW]     flag: workgroup g's SwiGLU rows of this layer are stored
+    uint32_t* hp;       // [L][T*K][F/16][kHBW] SwiGLU h as fp16 pairs: 8 hi words, then 8 lo words
     int lds_us, lds_part, lds_misc, lds_pre, lds_wr, lds_xh;
     // down-projection rows prefetched into LDS: up to pre_cap distinct
     // experts, each [rows][blocks][W] codes (pre_cstride bytes) followed by
@@ -48,11 +59,13 @@ __host__ __device__ inline int hloc_floats(int DPW, int T) {
     const int b = 16 * T * kMaxItemsInFlight;
     return a > b ? a : b;
 }
+// floats of the per-(wave, item, token, row) gate/up sums staged in LDS
+__host__ __device__ inline int gu_floats(int T) { return kMaxItemsInFlight * T * 4 * 8; }
 // byte offset (from the misc base) of the top-k candidate arrays, past
-// s_ids .. s_hres, 16-byte aligned
+// s_ids .. s_gu, 16-byte aligned
 __host__ __device__ inline int misc_tail_offset(int PT, int T, int DPW) {
     const int end = misc_head_bytes(PT, T) + 8 * 4 * kMaxEPW * T + 4 * hloc_floats(DPW, T) + 16 + 8 * 4 * T +
-                    4 * T * DPW;
+                    4 * T * DPW + 4 * gu_floats(T);
     return (end + 15) & ~15;
 }
 

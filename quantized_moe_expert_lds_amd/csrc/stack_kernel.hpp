@@ -7,37 +7,43 @@
 // ~15 MB, about 2 us of HBM time on MI355X, while a kernel launch with 256
 // workgroups costs ~3-4 us and a dependent launch in a graph ~1.6 us, so a
 // step is one cooperative launch with one workgroup per CU that stays
-// resident for all layers; grid barriers replace kernel boundaries.
+// resident for all layers.
 //
-// Per layer l, three phases separated by grid barriers:
+// Per layer l, three phases; each hands its results to the next through
+// device memory:
 //   ROUTE : u_l = h_l (l = 0) or RMSNorm(h_l), computed redundantly by every
-//           workgroup from the residual slices and sums of squares the
+//           workgroup from the residual rows and sums of squares the
 //           workgroups published; workgroup w then computes the fp64 logits
-//           of experts w*EPW .. from router rows it loaded during the previous
-//           layer.
-//   FFN   : every workgroup reads all logits, selects the top-k per token
+//           of experts w*EPW .. from router rows it copied into LDS during the
+//           previous layer, and publishes them.
+//   FFN   : every workgroup gathers all logits, selects the top-k per token
 //           (ties to the lower id), derives the distinct experts of the batch
 //           and processes its share of (expert, 16-row d_ff chunk) items:
-//           2-/3-bit unpack, fp16 dot products with fp32 accumulation,
-//           SwiGLU, fp16 h per (token, slot) pair.  While wave 0 waits at the
-//           next barrier, waves 1-3 copy the down-projection rows the
-//           workgroup needs next into LDS.
-//   DOWN  : workgroup w owns d_model rows w*DPW ..; it combines those rows of
-//           every distinct expert (blocks in order, slots in order with their
-//           gates), adds the residual and publishes its slice of h and its
-//           sum of squares.
+//           2-/3-bit unpack, dot products with fp32 accumulation, SwiGLU,
+//           h per (token, slot) pair; then it raises its flag.
+//   DOWN  : workgroup w owns d_model rows w*DPW ..; once every flag is up it
+//           combines those rows of every distinct expert (blocks in order,
+//           slots in order with their gates), adds the residual and
+//           publishes its rows of h and their sum of squares.
 //
-// Coherence.  Every buffer shared between workgroups exists once per layer,
-// so it is written once per launch, and every 128-byte line of it is written
-// by a single workgroup.  Writers use agent-scope (write-through) stores;
-// after a barrier readers use ordinary cached vector loads: a line can only
-// enter an L2 after its writer finished it, and kernel boundaries invalidate
-// the L2s.  A barrier is a relaxed agent-scope atomic add on one of 8
-// counters (one per XCD slot, 256 B apart) after each thread's stores have
-// completed, and a poll of the 8 counters by 8 lanes.  Every wait is bounded
-// by a wall-clock timeout: on expiry the kernel records an error flag and
+// Precision.  The activations u and the SwiGLU output h enter the packed
+// fp16 dot products as two fp16 halves (hi = fp16(v), lo = fp16(v - hi));
+// the levels are exact small integers and the accumulation is fp32, so the
+// dot products carry ~22 bits of u and h, close to an fp32 evaluation.
+//
+// Hand-over.  Logits and residual rows travel as tagged 64-bit words
+// (payload + epoch, one agent-scope atomic each; see ll_store): a reader
+// spins on exactly the words it needs until they carry this layer's epoch,
+// so no grid-wide barrier is needed and the data arrive with the signal.
+// The SwiGLU rows (many words read by every workgroup) are stored once per
+// layer and launch with write-through agent-scope stores into a buffer of
+// their own per layer, followed by the writer's tagged flag; readers load
+// them with ordinary cached loads after seeing every flag.  That relies on
+// the hardware rather than on the HIP memory model: a line of that buffer
+// enters a workgroup's L2 only after its writer's stores have completed,
+// and a kernel launch starts with invalidated L2s.  Every wait is bounded
+// by a wall-clock timeout: on expiry the kernel records an error word and
 // exits instead of hanging.
-#include "common.hpp"
 //
 // This header holds the kernel template; each stack_t<T>.hip instantiates it
 // for one batch size, so the instantiations compile in parallel.
@@ -86,17 +92,8 @@ struct LdsCopy {
     int bytes;
 };
 
-struct NoSideWork {
-    __device__ void operator()() const {}
-};
 
 // ------------------------------------------------------- coherent stores
-__device__ __forceinline__ void st_f32(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_f64(double* p, double v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -295,46 +292,74 @@ __device__ void wave_merge_topk(const double* cv, const int* ci, const unsigned*
     }
 }
 
-// Grid barrier number `epoch` (1-based).  Returns false if it timed out or
-// another workgroup reported an error.
-// Waves 1..3 may start an LDS copy (`cp`) while wave 0 waits; it completes
-// by the next barrier.
-// Waves 1-3 run `side` (copies into LDS) while wave 0 waits for the grid.
-template <typename Side = NoSideWork>
-__device__ bool grid_barrier(const StackParams& P, int epoch, int* s_flag, Side side = Side{}) {
-    // every thread waits until its own stores have completed (gfx9 counts
-    // stores in vmcnt; a workgroup-scope release fence emits no wait)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int* sync = P.sync;
-    if (threadIdx.x >= 64) side();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        if (lane == 0)
-            __hip_atomic_fetch_add(&sync[(blockIdx.x & 7) * kLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int ok = 1;
-        if (lane < 8) {
-            const int need = epoch * ((P.G - lane + 7) >> 3);
-            const long long t0 = wall_clock64();
-            int n = 0;
-            while (__hip_atomic_load(&sync[lane * kLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                if ((++n & 63) == 0 &&
-                    (__hip_atomic_load(&sync[9 * kLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
-                     wall_clock64() - t0 > kTimeoutTicks)) {
-                    ok = 0;
-                    break;
-                }
-            }
-        }
-        const unsigned long long bad = __ballot(lane < 8 && !ok);
-        if (lane == 0) {
-            if (bad) __hip_atomic_store(&sync[9 * kLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *s_flag = bad ? 0 : 1;
+// ------------------------------------------------------ tagged exchanges
+// A shared value travels as a 64-bit word: the 32-bit payload in the low
+// half and the epoch it belongs to in the high half, stored and loaded with
+// agent-scope atomics.  A reader waits until the word carries the epoch it
+// expects; payload and tag arrive together (one single-copy-atomic word), so
+// no fence or separate flag is needed, and the tag also tells this layer's
+// value from one left by an earlier layer or launch.  Every word of token
+// slot t is tagged with that slot's epoch base[t] + layer + 1; the bases
+// advance by L at the end of every launch that uses the slot, so a word
+// never carries a current tag before it is written in the current launch.
+__device__ __forceinline__ void ll_store(u64* p, uint32_t tag, uint32_t payload) {
+    __hip_atomic_store(p, ((u64)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ll_load(const u64* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// true once the wait must end: the wall-clock limit passed, or another
+// workgroup reported an error
+__device__ __forceinline__ bool stack_should_stop(const StackParams& P, long long t0) {
+    return __hip_atomic_load(&P.hdr[kHdrErr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+           wall_clock64() - t0 > kTimeoutTicks;
+}
+
+// Waits until the first n of the N words addr(i) carry tag tg(i) and returns
+// their payloads in out.  All loads are issued before any wait.  Returns
+// false if the wait had to stop (stack_should_stop).
+template <int N, typename Addr, typename Tag>
+__device__ __forceinline__ bool ll_wait(Addr addr, Tag tg, uint32_t (&out)[N], int n, const StackParams& P) {
+    u64 v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = i < n ? ll_load(addr(i)) : 0ull;
+    uint64_t pend = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (i < n && (uint32_t)(v[i] >> 32) != tg(i)) pend |= 1ull << i;
+    if (pend) {
+        const long long t0 = wall_clock64();
+        int it = 0;
+        while (pend) {
+            if ((++it & 15) == 0 && stack_should_stop(P, t0)) return false;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if ((pend >> i) & 1) v[i] = ll_load(addr(i));
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if (((pend >> i) & 1) && (uint32_t)(v[i] >> 32) == tg(i)) pend &= ~(1ull << i);
         }
     }
-    __syncthreads();
-    return *s_flag != 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = (uint32_t)v[i];
+    return true;
 }
+
+// Ends the kernel for the whole workgroup when any of its threads had to stop
+// waiting; the first such workgroup records the error for the caller.  The
+// workgroup's verdict goes through an LDS word that starts at zero and is
+// only ever set (a workgroup that sees it set exits).
+#define STACK_CHECK_OK(ok)                                                                           \
+    do {                                                                                             \
+        if (!(ok)) s_misc[1] = 1;                                                                    \
+        __syncthreads();                                                                             \
+        if (s_misc[1]) {                                                                             \
+            if (threadIdx.x == 0)                                                                    \
+                __hip_atomic_store(&P.hdr[kHdrErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+            return;                                                                                  \
+        }                                                                                            \
+    } while (0)
 
 // NB bits of the 96-bit string w[0] | w[1] << 32 | w[2] << 64 from bit p
 // (compile-time p after unrolling); bits past 96 read as zero
@@ -419,18 +444,33 @@ __device__ __forceinline__ void levels16(const uint32_t* w, uint32_t* lv, const 
     }
 }
 
-__device__ __forceinline__ float dot16h(const uint32_t* lv, const uint32_t* xp) {
+// Dot product of a block's levels with an operand split into fp16 halves v =
+// hi + lo (hi = fp16(v), lo = fp16(v - hi)): the levels are exact small
+// integers, so this carries ~22 significant bits of v into the fp32
+// accumulation.  The small lo terms are summed first.
+__device__ __forceinline__ float dot32h(const uint32_t* lv, const uint32_t* hi, const uint32_t* lo) {
     float acc = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_fdot2(as_half2(lv[m]), as_half2(xp[m]), acc, false);
+    for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_fdot2(as_half2(lv[m]), as_half2(lo[m]), acc, false);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_fdot2(as_half2(lv[m]), as_half2(hi[m]), acc, false);
     return acc;
+}
+
+// v = hi + lo with hi = fp16(v) and lo = fp16(v - hi) (v - hi is exact in fp32)
+__device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
+    hi = (_Float16)v;
+    lo = (_Float16)(v - (float)hi);
 }
 
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
-// u as fp16 in unpack order, one 17-word row per 32-element block (16 pair
-// words + 1 pad word, so lane-per-block reads hit distinct banks).  Element
-// i of a block sits in pair word (i & 16) / 2 + (i & 7), half (i >> 3) & 1.
+// u in LDS as fp16 halves in unpack order, one kXhWords-word row per
+// (token, 32-element block): words 0..15 hold the hi pairs, 16..31 the lo
+// pairs.  The 144-byte row stride keeps the 16-byte reads of a lane per block
+// on distinct banks.  Element i of a block sits in pair word
+// (i & 16) / 2 + (i & 7), half (i >> 3) & 1; this returns the half index of
+// its hi part (the lo part is 32 halves further).
 __device__ __forceinline__ int xh_half_index(int t, int nkb, int d) {
     const int kb = d >> 5, i = d & 31;
     return ((t * nkb + kb) * kXhWords + ((i >> 4) << 3) + (i & 7)) * 2 + ((i >> 3) & 1);
@@ -450,7 +490,7 @@ __device__ __forceinline__ void load_block(const uint32_t* qb, size_t blk, uint3
 }
 
 
-template <int T, int BITS, int KPER>
+template <int T, int BITS, int KPER, int EPWM>
 __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P) {
     constexpr int W = BITS == 2 ? 2 : 3;
     extern __shared__ __align__(16) unsigned char lds[];
@@ -466,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     const int d_lo = min(w * DPW, D), d_hi = min(d_lo + DPW, D);
     const int nrows = d_hi - d_lo;
 
-    _Float16* xh = reinterpret_cast<_Float16*>(lds + P.lds_xh);           // [T][D/32][17 words]
+    _Float16* xh = reinterpret_cast<_Float16*>(lds + P.lds_xh);           // [T][D/32][kXhWords]
     const uint32_t* xhw = reinterpret_cast<const uint32_t*>(lds + P.lds_xh);
     float* part = reinterpret_cast<float*>(lds + P.lds_part);             // [PT][DPW][nkbF]
     double* s_z = reinterpret_cast<double*>(lds + P.lds_part);            // [T][E] (dead before part is used)
@@ -478,19 +518,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     int* s_uniq = reinterpret_cast<int*>(s_gates + PT);                   // [PT]
     int* s_first = s_uniq + PT;                                           // [PT]
     short* s_upair = reinterpret_cast<short*>(s_first + PT);              // [PT][T]
-    double* s_red = reinterpret_cast<double*>(misc + misc_head_bytes(PT, T));   // [4][kMaxEPW][T]
-    float* s_hloc = reinterpret_cast<float*>(s_red + 4 * kMaxEPW * T);    // see hloc_floats
-    int* s_misc = reinterpret_cast<int*>(s_hloc + hloc_floats(DPW, T));   // [0] = U, [1] = flag
+    double* s_red = reinterpret_cast<double*>(misc + misc_head_bytes(PT, T));   // [4][EPWM][T]
+    float* s_hloc = reinterpret_cast<float*>(s_red + 4 * EPWM * T);    // see hloc_floats
+    int* s_misc = reinterpret_cast<int*>(s_hloc + hloc_floats(DPW, T));   // [0] = U
     double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [4][T] per-wave sums of squares
     float* s_hres = reinterpret_cast<float*>(s_r + 4 * T);                // [T][DPW] own residual rows
+    float* s_gu = s_hres + T * DPW;                                       // see gu_floats
     double* s_cand_v = reinterpret_cast<double*>(misc + misc_tail_offset(PT, T, DPW));   // [256] top-k lists
     int* s_cand_i = reinterpret_cast<int*>(s_cand_v + 256);               // [256]
     unsigned* s_cand_k = reinterpret_cast<unsigned*>(s_cand_i + 256);     // [256]
 
-    const size_t zb_layer = (size_t)G * T * kZW;
-    const size_t hb_layer = (size_t)G * T * kHW;
-    const size_t sb_layer = (size_t)G * 16;
     const size_t hp_layer = (size_t)PT * nch * kHBW;
+
+    // epoch of token slot t at layer l; flags of a layer carry slot 0's epoch
+    uint32_t base[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) base[t] = P.hdr[kHdrBase + t];
 
     // router rows of this workgroup's experts live in LDS, copied by DMA one
     // layer ahead (expert-major rows are contiguous)
@@ -504,6 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         const LdsCopy c = router_copy(0);
         dma_to_lds(c.src, c.dst, c.bytes, 0, 4);
     }
+    if (tid == 0) s_misc[1] = 0;
     for (int i = tid; i < T * nrows; i += kThreads) {
         const int t = i / nrows, r = i - t * nrows;
         const size_t xi = (size_t)t * D + d_lo + r;
@@ -512,51 +556,78 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    int epoch = 0;
     for (int l = 0; l < L; ++l) {
         // ------------------------------------------------------------- ROUTE
         float bias_v = 0.0f;           // bias of (expert j, token t) for thread j*T + t
-        if (m.router_b && tid < kMaxEPW * T) {
+        if (m.router_b && tid < EPWM * T) {
             const int j = tid / T, e = w * EPW + j;
             if (j < EPW && e < E) bias_v = m.router_b[(size_t)l * E + e];
         }
         {
-            // Thread tid owns elements d = tid + 256 k of every token: it loads
-            // them (x, or the residual slices the workgroups published), forms
-            // u, stores u's fp16 pairs for the expert phase and accumulates its
-            // share of this workgroup's logits, with no barrier in between.
-            const float* hbp = P.hb + (size_t)(l > 0 ? l - 1 : 0) * hb_layer;
-            constexpr int KR = T >= 16 ? 1 : 16 / T;      // elements per token per round of loads
+            // Thread tid owns elements d = tid + 256 k of every token: it waits
+            // for them (x, or the residual rows the workgroups published),
+            // forms u, stores u's fp16 halves for the expert phase and
+            // accumulates its share of this workgroup's logits.
+            constexpr int KR = T >= 8 ? 2 : (T >= 4 ? 4 : 8);   // elements per token per round of waits
             float hv[KR][T];
-            auto load_round = [&](int k0) {
+            bool ok = true;
+            // tagged words of the residual rows (written by layer l - 1)
+            auto row_word = [&](int k0, int i) -> const u64* {
+                const int kr = i / T, t = i - kr * T;
+                const int d = min(tid + (k0 + kr) * kThreads, D - 1);
+                const int g = d / DPW;
+                return P.sl + ((size_t)g * kSlots + t) * kSLW + (d - g * DPW);
+            };
+            auto row_tag = [&](int i) { return base[i % T] + (uint32_t)l; };
+            auto take_rows = [&](const uint32_t* pay) {
+#pragma unroll
+                for (int kr = 0; kr < KR; ++kr)
+#pragma unroll
+                    for (int t = 0; t < T; ++t) hv[kr][t] = __uint_as_float(pay[kr * T + t]);
+            };
+            auto load_x = [&](int k0) {
 #pragma unroll
                 for (int kr = 0; kr < KR; ++kr) {
                     const int d = min(tid + (k0 + kr) * kThreads, D - 1);
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
-                        if (l == 0) {
-                            const size_t xi = (size_t)t * D + d;
-                            hv[kr][t] = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[xi]) : ((const float*)P.x)[xi];
-                        } else {
-                            const int g = d / DPW;
-                            hv[kr][t] = hbp[((size_t)g * T + t) * kHW + (d - g * DPW)];
-                        }
+                        const size_t xi = (size_t)t * D + d;
+                        hv[kr][t] = P.x_bf16 ? bf16_to_f32(((const uint16_t*)P.x)[xi]) : ((const float*)P.x)[xi];
                     }
                 }
             };
-            load_round(0);                                // in flight during the sums of squares
             double rr[T], inv[T];
             if (l > 0) {
-                // sums of squares: thread g loads workgroup g's sum (threads
-                // over workgroups, then DPP, then the 4 waves in order); every
-                // thread then forms the same rms from the 4 wave sums
-                const double* sbp = P.sb + (size_t)(l - 1) * sb_layer;
+                // sums of squares: thread g waits for workgroup g's (threads
+                // over workgroups, then DPP, then the 4 waves in order), in
+                // the same wait as its first round of rows; every thread then
+                // forms the same rms from the 4 wave sums
                 double ss[T];
+                {
+                    const int g = tid;
+                    const int nss = g < G ? 2 * T : 0;
+                    uint32_t pay[2 * T + KR * T];
+                    ok = ll_wait<2 * T + KR * T>(
+                        [&](int i) -> const u64* {
+                            if (i < 2 * T) return P.sl + ((size_t)min(g, G - 1) * kSlots + (i >> 1)) * kSLW + kSSWord + (i & 1);
+                            return row_word(0, i - 2 * T);
+                        },
+                        [&](int i) { return i < 2 * T ? base[i >> 1] + (uint32_t)l : row_tag(i - 2 * T); },
+                        pay, 2 * T + KR * T, P);
 #pragma unroll
-                for (int t = 0; t < T; ++t) ss[t] = tid < G ? sbp[(size_t)tid * 16 + t] : 0.0;
-                for (int g = tid + kThreads; g < G; g += kThreads)
+                    for (int t = 0; t < T; ++t)
+                        ss[t] = nss ? __hiloint2double((int)pay[2 * t + 1], (int)pay[2 * t]) : 0.0;
+                    take_rows(pay + 2 * T);
+                }
+                for (int g = tid + kThreads; g < G; g += kThreads) {
+                    uint32_t pay[2 * T];
+                    ok = ok && ll_wait<2 * T>(
+                        [&](int i) -> const u64* { return P.sl + ((size_t)g * kSlots + (i >> 1)) * kSLW + kSSWord + (i & 1); },
+                        [&](int i) { return base[i >> 1] + (uint32_t)l; }, pay, 2 * T, P);
 #pragma unroll
-                    for (int t = 0; t < T; ++t) ss[t] += sbp[(size_t)g * 16 + t];
+                    for (int t = 0; t < T; ++t) ss[t] += __hiloint2double((int)pay[2 * t + 1], (int)pay[2 * t]);
+                }
+                STACK_CHECK_OK(ok);
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const double v = wave_sum_f64(ss[t]);
@@ -569,14 +640,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     rr[t] = sqrt(tot / (double)D + P.eps);
                     inv[t] = 1.0 / rr[t];
                 }
+            } else {
+                load_x(0);
             }
-            double acc[kMaxEPW][T];
+            double acc[EPWM][T];
 #pragma unroll
-            for (int j = 0; j < kMaxEPW; ++j)
+            for (int j = 0; j < EPWM; ++j)
 #pragma unroll
                 for (int t = 0; t < T; ++t) acc[j][t] = 0.0;
             for (int k0 = 0; k0 * kThreads < D; k0 += KR) {
-                if (k0 > 0) load_round(k0);
+                if (k0 > 0) {
+                    if (l == 0) {
+                        load_x(k0);
+                    } else {
+                        uint32_t pay[KR * T];
+                        ok = ll_wait<KR * T>([&](int i) { return row_word(k0, i); }, row_tag, pay, KR * T, P);
+                        STACK_CHECK_OK(ok);
+                        take_rows(pay);
+                    }
+                }
 #pragma unroll
                 for (int kr = 0; kr < KR; ++kr) {
                     const int d = tid + (k0 + kr) * kThreads;
@@ -591,75 +673,67 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                             const double q0 = hd * inv[t];
                             uv = (float)fma(fma(-q0, rr[t], hd), inv[t], q0);
                         }
-                        xh[xh_half_index(t, nkbD, d)] = (_Float16)uv;
+                        _Float16 uh, ul;
+                        split_f16(uv, uh, ul);
+                        const int xi = xh_half_index(t, nkbD, d);
+                        xh[xi] = uh;
+                        xh[xi + 32] = ul;
 #pragma unroll
-                        for (int j = 0; j < kMaxEPW; ++j)
+                        for (int j = 0; j < EPWM; ++j)
                             if (j < my_experts) acc[j][t] = fma((double)uv, (double)wr_lds[j * D + d], acc[j][t]);
                     }
                 }
             }
 #pragma unroll
-            for (int j = 0; j < kMaxEPW; ++j) {
+            for (int j = 0; j < EPWM; ++j) {
                 if (j >= EPW) break;
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const double v = wave_sum_f64(acc[j][t]);
-                    if (lane == 0) s_red[(wave * kMaxEPW + j) * T + t] = v;
+                    if (lane == 0) s_red[(wave * EPWM + j) * T + t] = v;
                 }
             }
             __syncthreads();
-            if (tid < kMaxEPW * T) {
+            if (tid < EPWM * T) {
                 const int j = tid / T, t = tid - j * T;
                 const int e = w * EPW + j;
                 if (j < EPW && e < E) {
-                    double s = ((s_red[(0 * kMaxEPW + j) * T + t] + s_red[(1 * kMaxEPW + j) * T + t]) +
-                                s_red[(2 * kMaxEPW + j) * T + t]) + s_red[(3 * kMaxEPW + j) * T + t];
+                    double s = ((s_red[(0 * EPWM + j) * T + t] + s_red[(1 * EPWM + j) * T + t]) +
+                                s_red[(2 * EPWM + j) * T + t]) + s_red[(3 * EPWM + j) * T + t];
                     s += (double)bias_v;
-                    st_f64(&P.zb[(size_t)l * zb_layer + ((size_t)w * T + t) * kZW + j], s);
+                    u64* q = P.lg + ((size_t)w * kSlots + t) * kLGW + 2 * j;
+                    const uint32_t tg = base[t] + (uint32_t)l + 1u;
+                    ll_store(q, tg, (uint32_t)__double2loint(s));
+                    ll_store(q + 1, tg, (uint32_t)__double2hiint(s));
                 }
             }
         }
-        // the next layer's router rows stream in while this barrier waits
-        // (every wave is done reading wr_lds once the barrier's entry
-        // __syncthreads has passed)
-        if (!grid_barrier(P, ++epoch, &s_misc[1], [&]() {
-                if (l + 1 < L && my_experts > 0) {
-                    const LdsCopy c = router_copy(l + 1);
-                    dma_to_lds(c.src, c.dst, c.bytes, 1, 3);
-                }
-            }))
-            return;
 
         // --------------------------------------------------------------- FFN
         {
-            // logit lines (workgroup g, token t), all loads of a round in flight
-            const double* zbp = P.zb + (size_t)l * zb_layer;
-            const int nz = G * T;
-            for (int i0 = 0; i0 < nz; i0 += 4 * kThreads) {
-                double2 v[4][2];
+            // logits of every expert: thread g waits for workgroup g's line,
+            // two experts (four words) per token at a time
+            bool ok = true;
+            for (int g = tid; g < G; g += kThreads) {
+                const int ne = min(EPW, E - g * EPW);
+                for (int j0 = 0; j0 < ne; j0 += 2) {
+                    const int nj = min(2, ne - j0);
+                    uint32_t pay[4 * T];
+                    ok = ok && ll_wait<4 * T>(
+                        [&](int i) -> const u64* {
+                            const int t = i >> 2, k4 = min(i & 3, 2 * nj - 1);
+                            return P.lg + ((size_t)g * kSlots + t) * kLGW + 2 * j0 + k4;
+                        },
+                        [&](int i) { return base[i >> 2] + (uint32_t)l + 1u; }, pay, 4 * T, P);
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int i = min(i0 + tid + a * kThreads, nz - 1);
-                    const double2* src = reinterpret_cast<const double2*>(zbp + (size_t)i * kZW);
-                    v[a][0] = src[0];
-                    v[a][1] = src[1];
-                }
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int i = i0 + tid + a * kThreads;
-                    if (i < nz) {
-                        const int g = i / T, t = i - g * T;
-                        const double vv[4] = {v[a][0].x, v[a][0].y, v[a][1].x, v[a][1].y};
-#pragma unroll
-                        for (int j = 0; j < kMaxEPW; ++j) {
-                            const int e = g * EPW + j;
-                            if (j < EPW && e < E) s_z[t * E + e] = vv[j];
-                        }
-                    }
+                    for (int t = 0; t < T; ++t)
+                        for (int j = 0; j < nj; ++j)
+                            s_z[t * E + g * EPW + j0 + j] =
+                                __hiloint2double((int)pay[4 * t + 2 * j + 1], (int)pay[4 * t + 2 * j]);
                 }
             }
+            STACK_CHECK_OK(ok);
         }
-        __syncthreads();
         constexpr bool kSplitTopk = T == 1 && KPER >= 4;
         const bool split_topk = kSplitTopk && 4 * K <= 64;
         if (split_topk) {
@@ -763,12 +837,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         const int uid = lane < U ? s_uniq[lane] : 0;     // distinct expert `lane` (first 64)
         const int n_pre = min(U, P.pre_cap);
         // copy this workgroup's down-projection rows d_lo .. d_hi of the first
-        // n_pre distinct experts into LDS.  Waves 1-3 issue the copies while
-        // wave 0 waits at the next grid barrier, so they do not compete with
-        // the gate/up weight loads; chunks are dealt to the three waves
+        // n_pre distinct experts (and the next layer's router rows) into LDS.
+        // Waves 1-3 issue the copies while wave 0 waits for the other
+        // workgroups' SwiGLU flags; chunks are dealt to the three waves
         // round-robin.  Wave-uniform control flow only: every lane of the
         // wave takes part in a chunk.
         auto issue_down_prefetch = [&]() {
+            if (l + 1 < L && my_experts > 0) {
+                const LdsCopy c = router_copy(l + 1);
+                dma_to_lds(c.src, c.dst, c.bytes, 1, 3);
+            }
             if (nrows <= 0) return;
             const int cbytes = nrows * nkbF * W * 4, sbytes = nrows * nkbF * 2;
             int ci = 0;
@@ -788,13 +866,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         {
             const int n_items = U * nch;
             const size_t lstrideGU = (size_t)E * F * nkbD;
-            uint32_t xp0[T][16];                    // x pairs of block kb = lane (clamped), read once
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int mm = 0; mm < 16; ++mm) xp0[t][mm] = xhw[(t * nkbD + min(lane, nkbD - 1)) * kXhWords + mm];
+            const bool kact = lane < nkbD;                    // d_model <= 2048: one block per lane
+            const int kbc = kact ? lane : nkbD - 1;           // loads stay in bounds
             for (int it0 = w; it0 < n_items; it0 += G * kMaxItemsInFlight) {
-                float acc[kMaxItemsInFlight][8][T];
                 int tmask[kMaxItemsInFlight];       // tokens that chose the item's expert
                 int ie[kMaxItemsInFlight];          // the item's expert
 #pragma unroll
@@ -810,81 +884,73 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     tmask[a] = __builtin_amdgcn_readfirstlane(msk);
                     ie[a] = __builtin_amdgcn_readfirstlane(e);
                 }
-#pragma unroll
-                for (int a = 0; a < kMaxItemsInFlight; ++a)
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-#pragma unroll
-                        for (int t = 0; t < T; ++t) acc[a][r][t] = 0.0f;
-                for (int kb0 = 0; kb0 < nkbD; kb0 += 64) {        // wave-uniform loop
-                    const int kb = kb0 + lane;
-                    const bool kact = kb < nkbD;
-                    const int kbc = kact ? kb : nkbD - 1;         // loads stay in bounds
-                    uint32_t q[kMaxItemsInFlight][8][W];
-                    uint16_t sr[kMaxItemsInFlight][8];
-#pragma unroll
-                    for (int a = 0; a < kMaxItemsInFlight; ++a) {
-                        const int it = it0 + a * G;
-                        if (it >= n_items) continue;
-                        const int c = it - (it / nch) * nch;
-                        const int f0 = 16 * c + 4 * wave;
-#pragma unroll
-                        for (int r = 0; r < 8; ++r) {
-                            const size_t blk = (size_t)l * lstrideGU + ((size_t)ie[a] * F + f0 + (r & 3)) * nkbD + kbc;
-                            load_block<W>(r < 4 ? m.gate_q : m.up_q, blk, q[a][r]);
-                            sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
-                        }
-                    }
-                    if (gates_pending) {
-                        gates_pending = false;
-                        if (wave == 0) finish_gates();
-                    }
-                    uint32_t xpk[T][16];
-                    if (kb0 > 0) {
-#pragma unroll
-                        for (int t = 0; t < T; ++t)
-#pragma unroll
-                            for (int mm = 0; mm < 16; ++mm) xpk[t][mm] = xhw[(t * nkbD + kbc) * kXhWords + mm];
-                    }
-                    // every loaded register is consumed on every path (lanes past
-                    // the last block add 0), so no load is left in flight at the
-                    // loop's back edge
-#pragma unroll
-                    for (int a = 0; a < kMaxItemsInFlight; ++a) {
-                        if (it0 + a * G >= n_items) continue;
-#pragma unroll
-                        for (int r = 0; r < 8; ++r) {
-                            uint32_t lv[16];
-                            levels16<BITS>(q[a][r], lv, uk);
-                            const float sc = kact ? h2f(sr[a][r]) : 0.0f;
-#pragma unroll
-                            for (int t = 0; t < T; ++t)        // (one token: it chose every item's expert)
-                                if (T == 1 || ((tmask[a] >> t) & 1))
-                                    acc[a][r][t] = fmaf(sc, dot16h(lv, kb0 == 0 ? xp0[t] : xpk[t]), acc[a][r][t]);
-                        }
-                    }
-                }
-                // wave sums, gathered so lane j = (a T + t) 4 + r holds the
-                // gate and up sums of (item a, token t, row r); one SwiGLU
-                // evaluation then covers all of them
-                static_assert(4 * T * kMaxItemsInFlight <= 64, "one lane per (item, token, row)");
-                float gv = 0.0f, uv = 0.0f;
+                uint32_t q[kMaxItemsInFlight][8][W];
+                uint16_t sr[kMaxItemsInFlight][8];
 #pragma unroll
                 for (int a = 0; a < kMaxItemsInFlight; ++a) {
                     const int it = it0 + a * G;
                     if (it >= n_items) continue;
+                    const int c = it - (it / nch) * nch;
+                    const int f0 = 16 * c + 4 * wave;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
+                    for (int r = 0; r < 8; ++r) {
+                        const size_t blk = (size_t)l * lstrideGU + ((size_t)ie[a] * F + f0 + (r & 3)) * nkbD + kbc;
+                        load_block<W>(r < 4 ? m.gate_q : m.up_q, blk, q[a][r]);
+                        sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
+                    }
+                }
+                if (gates_pending) {
+                    gates_pending = false;
+                    if (wave == 0) finish_gates();
+                }
+                // Gate and up sums of (item a, token t, row r) are formed one
+                // token at a time by the same instruction sequence for every
+                // batch size (the block products rounded on their own, never
+                // fused into a later add), so a token's sums do not depend on
+                // the batch.  They are gathered so lane (a T + t) 4 + r holds
+                // the pair for row r, and one SwiGLU evaluation covers them
+                // all.  Lanes past the last block use a zero scale.
+                static_assert(4 * T * kMaxItemsInFlight <= 64, "one lane per (item, token, row)");
+                float gv = 0.0f, uv = 0.0f;
+                {
+                    // token by token: its u halves from LDS (8 16-byte reads
+                    // per lane), the levels unpacked for each token that chose
+                    // the item's expert; sums staged in LDS
+                    float* gu = s_gu + wave * (kMaxItemsInFlight * T * 8);
 #pragma unroll
-                        for (int t = 0; t < T; ++t) {
-                            if (T > 1 && !((tmask[a] >> t) & 1)) continue;
-                            const float g = wave_sum_f32(acc[a][r][t]);
-                            const float uu = wave_sum_f32(acc[a][4 + r][t]);
-                            if (lane == (a * T + t) * 4 + r) {
-                                gv = g;
-                                uv = uu;
+                    for (int t = 0; t < T; ++t) {
+                        bool any = false;
+#pragma unroll
+                        for (int a = 0; a < kMaxItemsInFlight; ++a)
+                            any = any || (it0 + a * G < n_items && ((tmask[a] >> t) & 1));
+                        if (!any) continue;
+                        uint32_t xt[32];
+#pragma unroll
+                        for (int q4 = 0; q4 < 8; ++q4) {
+                            const uint4 v = *reinterpret_cast<const uint4*>(xhw + (t * nkbD + kbc) * kXhWords + 4 * q4);
+                            xt[4 * q4] = v.x;
+                            xt[4 * q4 + 1] = v.y;
+                            xt[4 * q4 + 2] = v.z;
+                            xt[4 * q4 + 3] = v.w;
+                        }
+#pragma unroll
+                        for (int a = 0; a < kMaxItemsInFlight; ++a) {
+                            if (it0 + a * G >= n_items || !((tmask[a] >> t) & 1)) continue;
+#pragma unroll
+                            for (int r = 0; r < 8; ++r) {
+                                uint32_t lv[16];
+                                levels16<BITS>(q[a][r], lv, uk);
+                                const float sc = kact ? h2f(sr[a][r]) : 0.0f;
+                                const float s = wave_sum_f32(__fmul_rn(sc, dot32h(lv, xt, xt + 16)));
+                                if (lane == 0) gu[(a * T + t) * 8 + r] = s;
                             }
                         }
+                    }
+                    const int a = lane / (4 * T), t = (lane >> 2) % T, r = lane & 3;
+                    if (a < kMaxItemsInFlight && it0 + a * G < n_items && ((tmask[a] >> t) & 1)) {
+                        gv = gu[(a * T + t) * 8 + r];
+                        uv = gu[(a * T + t) * 8 + 4 + r];
+                    }
                 }
                 {
                     const int a = lane / (4 * T), t = (lane >> 2) % T, r = lane & 3;
@@ -903,8 +969,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         const int u = it / nch, c = it - u * nch;
                         const int pr = s_upair[u * T + t];
                         if (pr >= 0) {
-                            half2_t hv = {(_Float16)s_hloc[(a * T + t) * 16 + mm], (_Float16)s_hloc[(a * T + t) * 16 + mm + 8]};
-                            st_u32(&P.hp[(size_t)l * hp_layer + ((size_t)pr * nch + c) * kHBW + mm], as_u32(hv));
+                            _Float16 h0, l0, h1, l1;
+                            split_f16(s_hloc[(a * T + t) * 16 + mm], h0, l0);
+                            split_f16(s_hloc[(a * T + t) * 16 + mm + 8], h1, l1);
+                            uint32_t* dst = P.hp + (size_t)l * hp_layer + ((size_t)pr * nch + c) * kHBW;
+                            st_u32(dst + mm, as_u32(half2_t{h0, h1}));
+                            st_u32(dst + 8 + mm, as_u32(half2_t{l0, l1}));
                         }
                     }
                 }
@@ -912,76 +982,96 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
         }
         if (gates_pending && wave == 0) finish_gates();   // workgroups without gate/up items
-        // the copies must have landed before any wave reads them after the barrier
-        if (!grid_barrier(P, ++epoch, &s_misc[1], [&]() {
-                issue_down_prefetch();
-                __builtin_amdgcn_s_waitcnt(0);
-            }))
-            return;
+        // this workgroup's SwiGLU rows of layer l are stored (every thread's
+        // write-through stores have completed): raise its flag
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) ll_store(P.fl + (size_t)w * kFLW, base[0] + (uint32_t)l + 1u, 1u);
 
         // -------------------------------------------------------------- DOWN
         {
+            // wave 0 waits for every workgroup's flag while waves 1-3 copy the
+            // down rows (and the next router rows) into LDS
+            bool ok = true;
+            if (wave == 0) {
+                for (int g0 = 0; g0 < G; g0 += 4 * 64) {
+                    uint32_t pay[4];
+                    ok = ok && ll_wait<4>(
+                        [&](int i) -> const u64* { return P.fl + (size_t)min(g0 + lane + 64 * i, G - 1) * kFLW; },
+                        [&](int i) { return base[0] + (uint32_t)l + 1u; }, pay, 4, P);
+                }
+            } else {
+                issue_down_prefetch();
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            STACK_CHECK_OK(ok);
+        }
+        {
             const uint32_t* hpp = P.hp + (size_t)l * hp_layer;
+            constexpr int kTG = T <= 2 ? T : 2;     // tokens whose h halves are held at once
             for (int it = tid; it < U * nkbF; it += kThreads) {
                 const int u = it / nkbF, kb = it - u * nkbF;
                 const int e = s_uniq[u];
-                uint32_t hv[T][16];
+                const bool in_lds = u < n_pre;
+                const char* cb = reinterpret_cast<const char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
+                const uint32_t* cw = reinterpret_cast<const uint32_t*>(cb);
+                const uint16_t* sw = reinterpret_cast<const uint16_t*>(cb + P.pre_cstride);
+                for (int t0 = 0; t0 < T; t0 += kTG) {
+                    int prs[kTG];
+                    bool any = false;
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const int pr = s_upair[u * T + t];
-                    if (pr < 0) continue;
-                    // block kb of d_ff = 16-row chunks 2kb (pairs 0..7) and 2kb+1 (pairs 8..15)
-                    const uint4* s0 = reinterpret_cast<const uint4*>(hpp + ((size_t)pr * nch + 2 * kb) * kHBW);
-                    const uint4* s1 = reinterpret_cast<const uint4*>(hpp + ((size_t)pr * nch + 2 * kb + 1) * kHBW);
-                    const uint4 a0 = s0[0], a1 = s0[1], b0 = s1[0], b1 = s1[1];
-                    hv[t][0] = a0.x; hv[t][1] = a0.y; hv[t][2] = a0.z; hv[t][3] = a0.w;
-                    hv[t][4] = a1.x; hv[t][5] = a1.y; hv[t][6] = a1.z; hv[t][7] = a1.w;
-                    hv[t][8] = b0.x; hv[t][9] = b0.y; hv[t][10] = b0.z; hv[t][11] = b0.w;
-                    hv[t][12] = b1.x; hv[t][13] = b1.y; hv[t][14] = b1.z; hv[t][15] = b1.w;
-                }
-                if (u < n_pre) {
-                    // rows from LDS (nrows <= 8 whenever experts are prefetched)
-                    const char* cb = reinterpret_cast<const char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
-                    const uint32_t* cw = reinterpret_cast<const uint32_t*>(cb);
-                    const uint16_t* sw = reinterpret_cast<const uint16_t*>(cb + P.pre_cstride);
+                    for (int tt = 0; tt < kTG; ++tt) {
+                        prs[tt] = t0 + tt < T ? s_upair[u * T + t0 + tt] : -1;
+                        any = any || prs[tt] >= 0;
+                    }
+                    if (!any) continue;
+                    uint32_t hv[kTG][32];               // hi pairs 0..15, lo pairs 16..31
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        if (r >= nrows) continue;
-                        uint32_t qv[W];
+                    for (int tt = 0; tt < kTG; ++tt) {
+                        if (prs[tt] < 0) continue;
+                        // block kb of d_ff = 16-row chunks 2kb (pairs 0..7) and 2kb+1 (pairs 8..15)
 #pragma unroll
-                        for (int k = 0; k < W; ++k) qv[k] = cw[(r * nkbF + kb) * W + k];
-                        const float sc = h2f(sw[r * nkbF + kb]);
-                        uint32_t lv[16];
-                        levels16<BITS>(qv, lv, uk);
+                        for (int hc = 0; hc < 2; ++hc) {
+                            const uint4* s0 =
+                                reinterpret_cast<const uint4*>(hpp + ((size_t)prs[tt] * nch + 2 * kb + hc) * kHBW);
+                            const uint4 a0 = s0[0], a1 = s0[1], b0 = s0[2], b1 = s0[3];
+                            const uint32_t v[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                                    b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-                        for (int t = 0; t < T; ++t) {
-                            const int pr = s_upair[u * T + t];
-                            if (pr < 0) continue;
-                            part[((size_t)pr * DPW + r) * nkbF + kb] = sc * dot16h(lv, hv[t]);
+                            for (int i = 0; i < 8; ++i) {
+                                hv[tt][8 * hc + i] = v[i];
+                                hv[tt][16 + 8 * hc + i] = v[8 + i];
+                            }
                         }
                     }
-                } else {
                     for (int r0 = 0; r0 < nrows; r0 += 8) {
-                        uint32_t q[8][W];
-                        uint16_t sr[8];
+                        uint32_t qd[8][W];
+                        float scd[8];
 #pragma unroll
-                        for (int r = 0; r < 8; ++r) {      // clamped rows: every load is issued unconditionally
+                        for (int r = 0; r < 8; ++r) {
+                            // rows from LDS when prefetched (nrows <= 8 then), else
+                            // clamped rows from memory: every load is issued
                             const int rr = min(r0 + r, nrows - 1);
-                            const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + rr) * nkbF + kb;
-                            load_block<W>(m.down_q, blk, q[r]);
-                            sr[r] = m.down_s[blk];
+                            if (in_lds) {
+#pragma unroll
+                                for (int k = 0; k < W; ++k) qd[r][k] = cw[(rr * nkbF + kb) * W + k];
+                                scd[r] = h2f(sw[rr * nkbF + kb]);
+                            } else {
+                                const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + rr) * nkbF + kb;
+                                load_block<W>(m.down_q, blk, qd[r]);
+                                scd[r] = h2f(m.down_s[blk]);
+                            }
                         }
 #pragma unroll
                         for (int r = 0; r < 8; ++r) {
                             if (r0 + r >= nrows) continue;
                             uint32_t lv[16];
-                            levels16<BITS>(q[r], lv, uk);
-                            const float sc = h2f(sr[r]);
+                            levels16<BITS>(qd[r], lv, uk);
 #pragma unroll
-                            for (int t = 0; t < T; ++t) {
-                                const int pr = s_upair[u * T + t];
-                                if (pr < 0) continue;
-                                part[((size_t)pr * DPW + r0 + r) * nkbF + kb] = sc * dot16h(lv, hv[t]);
+                            for (int tt = 0; tt < kTG; ++tt) {
+                                if (prs[tt] < 0) continue;
+                                part[((size_t)prs[tt] * DPW + r0 + r) * nkbF + kb] =
+                                    __fmul_rn(scd[r], dot32h(lv, hv[tt], hv[tt] + 16));
                             }
                         }
                     }
@@ -1014,20 +1104,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 float yv = 0.0f;
                 int j = 0;
                 for (; j + 8 <= K; j += 8) {
-                    float gv[8], ov[8];
+                    float gv8[8], ov[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        gv[i] = s_gates[t * K + j + i];
+                        gv8[i] = s_gates[t * K + j + i];
                         ov[i] = s_o[(t * K + j + i) * DPW + r];
                     }
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) yv = yv + gv[i] * ov[i];
+                    for (int i = 0; i < 8; ++i) yv = yv + gv8[i] * ov[i];
                 }
                 for (; j < K; ++j) yv = yv + s_gates[t * K + j] * s_o[(t * K + j) * DPW + r];
                 const int d = d_lo + r;
                 const float hn = s_hres[t * DPW + r] + yv;
                 s_hres[t * DPW + r] = hn;
-                if (l + 1 < L) st_f32(&P.hb[(size_t)l * hb_layer + ((size_t)w * T + t) * kHW + r], hn);
+                if (l + 1 < L) ll_store(P.sl + ((size_t)w * kSlots + t) * kSLW + r, base[t] + (uint32_t)l + 1u,
+                                        __float_as_uint(hn));
                 else P.h_out[(size_t)t * D + d] = hn;
                 if (P.h_layers) P.h_layers[((size_t)l * T + t) * D + d] = hn;
                 s_hloc[t * nrows + r] = hn;
@@ -1039,27 +1130,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     const double v = (double)s_hloc[tid * nrows + r];
                     ss += v * v;
                 }
-                st_f64(&P.sb[(size_t)l * sb_layer + (size_t)w * 16 + tid], ss);
+                u64* q = P.sl + ((size_t)w * kSlots + tid) * kSLW + kSSWord;
+                const uint32_t tg = base[tid] + (uint32_t)l + 1u;
+                ll_store(q, tg, (uint32_t)__double2loint(ss));
+                ll_store(q + 1, tg, (uint32_t)__double2hiint(ss));
             }
         }
-        if (l + 1 < L) {
-            if (!grid_barrier(P, ++epoch, &s_misc[1])) return;
-        }
     }
-    // last arrival resets the counters for the next launch
+    // the last workgroup to finish advances the epoch bases of the slots this
+    // launch used and resets the completion counter for the next launch
     __syncthreads();
     if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(&P.sync[8 * kLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == G - 1) {
-            for (int x = 0; x < 9; ++x)
-                __hip_atomic_store(&P.sync[x * kLine], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev =
+            __hip_atomic_fetch_add(&P.hdr[kHdrDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == (uint32_t)G - 1) {
+            for (int t = 0; t < T; ++t)
+                __hip_atomic_store(&P.hdr[kHdrBase + t], base[t] + (uint32_t)L, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&P.hdr[kHdrDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-template <int T, int BITS, int KPER>
+template <int T, int BITS, int KPER, int EPWM>
 hipError_t launch_stack_t(StackParams& P, size_t lds, hipStream_t s) {
-    auto fn = decode_stack_kernel<T, BITS, KPER>;
+    auto fn = decode_stack_kernel<T, BITS, KPER, EPWM>;
     // the dynamic LDS limit is raised once per device; two threads making
     // their first call at the same time both set the same value
     static std::atomic<int> attr_done[kMaxDevices];
@@ -1068,7 +1163,12 @@ hipError_t launch_stack_t(StackParams& P, size_t lds, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     if (!attr_done[dev].load(std::memory_order_acquire)) {
-        e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        // all of LDS the kernel's own (static) allocation leaves
+        hipFuncAttributes fa{};
+        e = hipFuncGetAttributes(&fa, (const void*)fn);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(kStackLdsLimit - fa.sharedSizeBytes));
         if (e != hipSuccess) return e;
         attr_done[dev].store(1, std::memory_order_release);
     }
@@ -1078,10 +1178,12 @@ hipError_t launch_stack_t(StackParams& P, size_t lds, hipStream_t s) {
 
 template <int T, int BITS>
 hipError_t launch_stack_e(StackParams& P, size_t lds, hipStream_t s) {
-    const int E = P.m.n_experts;
-    if (E <= 128) return launch_stack_t<T, BITS, 2>(P, lds, s);
-    if (E <= 512) return launch_stack_t<T, BITS, 8>(P, lds, s);
-    return launch_stack_t<T, BITS, 16>(P, lds, s);
+    // logits per lane in the top-k (KPER) and router experts per workgroup
+    // (EPWM) are compile-time bounds
+    const int E = P.m.n_experts, epw = (E + P.G - 1) / P.G;
+    if (E <= 128 && epw <= 2) return launch_stack_t<T, BITS, 2, 2>(P, lds, s);
+    if (E <= 512 && epw <= 2) return launch_stack_t<T, BITS, 8, 2>(P, lds, s);
+    return launch_stack_t<T, BITS, 16, kMaxEPW>(P, lds, s);
 }
 
 }  // namespace
