@@ -38,7 +38,7 @@ struct PrefillWs {
     size_t x16, hbuf, obuf, tiles, ntiles, total;
 };
 struct StackWs {
-    size_t sync, zbuf, hres, ssp, hbuf, total;
+    size_t hdr, rows, logits, flags, hp, total;
 };
 constexpr int kStackMaxGrid = 1024;      // workspace sized for up to this many workgroups
 constexpr int kStackMaxD = 2048;

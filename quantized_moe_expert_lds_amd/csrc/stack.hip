@@ -6,22 +6,23 @@ using namespace qmoe::stk;
 
 namespace qmoe {
 
-// Workspace: header, then the tagged residual-row, logit and flag buffers
-// (sized for kStackMaxGrid workgroups and kSlots token slots, so their
-// layout is the same for every batch size and device), then the per-layer
-// SwiGLU rows.
+// Workspace: header, then the tagged exchange buffers (sized for
+// kStackMaxGrid workgroups and kSlots token slots, so their layout is the
+// same for every batch size and device), then the per-layer SwiGLU rows.
+// Every 128-byte line of the exchange buffers is written by one workgroup
+// only (residual lines 256 B, logit lines of two slots, one flag line each).
 StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L) {
     StackWs w{};
     size_t off = 0;
-    w.sync = off;
+    w.hdr = off;
     off += kHdrBytes;
-    w.zbuf = off;                                              // residual rows + sums of squares
+    w.rows = off;                                              // residual rows + sums of squares
     off += align256(sizeof(u64) * (size_t)kStackMaxGrid * kSlots * kSLW);
-    w.hres = off;                                              // logits
+    w.logits = off;
     off += align256(sizeof(u64) * (size_t)kStackMaxGrid * kSlots * kLGW);
-    w.ssp = off;                                               // flags
+    w.flags = off;
     off += align256(sizeof(u64) * (size_t)kStackMaxGrid * kFLW);
-    w.hbuf = off;
+    w.hp = off;
     off += align256(sizeof(uint32_t) * (size_t)L * T * K * (F / 16) * kHBW);
     w.total = off;
     (void)D;
@@ -30,11 +31,9 @@ StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L) {
     return w;
 }
 
-// LDS plan of one workgroup.  Whatever the fixed regions leave of the LDS
-// limit holds prefetched down-projection rows, whole experts at a time.
+// LDS plan of one workgroup.
 struct StackLds {
-    size_t us, part, wr, xh, misc, pre, total;
-    int pre_cap, cstride, sstride, cgran, sgran;
+    size_t us, part, wr, xh, misc, total;
 };
 
 static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bits) {
@@ -42,13 +41,13 @@ static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bit
     const int DPW = (D + G - 1) / G;
     const int EPW = (E + G - 1) / G;
     const int PT = T * K;
-    const int W = bits == 2 ? 2 : 3;
     const int nkbF = F / 32;
+    (void)bits;
     size_t off = 0;
     p.us = off;                        // per-pair sums [PT][DPW] of the DOWN phase
     off += align256(sizeof(float) * (size_t)PT * DPW);
-    // ROUTE and FFN: logits [T][E] doubles, then u in fp16 pair order
-    // (padded); DOWN: per-block partial sums [PT][DPW][F/32] floats
+    // ROUTE and FFN: logits [T][E] doubles, then u as fp16 halves (padded
+    // rows); DOWN: per-block partial sums [PT][DPW][F/32] floats
     p.part = off;
     const size_t part_bytes = sizeof(float) * (size_t)PT * DPW * nkbF;
     const size_t z_bytes = align256(sizeof(double) * (size_t)T * E);
@@ -58,25 +57,10 @@ static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bit
     p.wr = off;                        // router rows
     off += align256(sizeof(float) * (size_t)EPW * D);
     p.misc = off;
-    size_t mb = (size_t)misc_head_bytes(PT, T);
-    mb = (size_t)misc_tail_offset(PT, T, DPW) + 256 * (sizeof(double) + 2 * sizeof(int));
-    off += align256(mb);
-    p.pre = off;
+    // top-k scratch: candidates (value, id, key) and selections (value, id),
+    // 64 per wave
+    off += align256((size_t)misc_tail_offset(PT, T, DPW) + 256 * (2 * sizeof(double) + 3 * sizeof(int)));
     p.total = off;
-    // prefetch: at most 8 rows per workgroup; copy granule 16 B where rows of
-    // codes / scales are multiples of 16 B, else 4 B; odd block counts are
-    // not prefetched
-    p.cstride = (int)((sizeof(uint32_t) * (size_t)DPW * nkbF * W + 15) & ~(size_t)15);
-    p.sstride = (int)((sizeof(uint16_t) * (size_t)DPW * nkbF + 15) & ~(size_t)15);
-    p.cgran = (nkbF * W) % 4 == 0 ? 16 : 4;
-    p.sgran = nkbF % 8 == 0 ? 16 : 4;
-    if (DPW <= 8 && nkbF % 2 == 0 && off < (size_t)kStackLdsLimit) {
-        const size_t per = (size_t)p.cstride + p.sstride;
-        size_t cap = ((size_t)kStackLdsLimit - off) / per;
-        if (cap > (size_t)PT) cap = PT;
-        p.pre_cap = (int)cap;
-        p.total = off + cap * per;
-    }
     return p;
 }
 
@@ -98,25 +82,17 @@ hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, 
     P.h_layers = h_layers;
     P.eps = eps;
     P.G = G;
-    P.hdr = (uint32_t*)(ws + L.sync);
-    P.sl = (u64*)(ws + L.zbuf);
-    P.lg = (u64*)(ws + L.hres);
-    P.fl = (u64*)(ws + L.ssp);
-    P.hp = (uint32_t*)(ws + L.hbuf);
+    P.hdr = (uint32_t*)(ws + L.hdr);
+    P.sl = (u64*)(ws + L.rows);
+    P.lg = (u64*)(ws + L.logits);
+    P.fl = (u64*)(ws + L.flags);
+    P.hp = (uint32_t*)(ws + L.hp);
     const StackLds pl = stack_lds_plan(T, m.d_model, m.d_ff, m.n_experts, m.top_k, G, m.bits);
     P.lds_us = (int)pl.us;
     P.lds_part = (int)pl.part;
     P.lds_wr = (int)pl.wr;
     P.lds_xh = (int)pl.xh;
     P.lds_misc = (int)pl.misc;
-    P.lds_pre = (int)pl.pre;
-    // prefetch needs 16-byte aligned rows for the 16-byte granule
-    const bool al = ((uintptr_t)m.down_q % 16 == 0) && ((uintptr_t)m.down_s % 16 == 0);
-    P.pre_cap = al ? pl.pre_cap : 0;
-    P.pre_cstride = pl.cstride;
-    P.pre_sstride = pl.sstride;
-    P.pre_cgran = pl.cgran;
-    P.pre_sgran = pl.sgran;
     const size_t lds = pl.total;
 #define QMOE_ST(N) \
     case N:           \

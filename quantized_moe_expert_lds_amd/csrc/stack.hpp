@@ -15,11 +15,11 @@ constexpr int kThreads = 256;
 constexpr int kSlots = 8;              // token slots of the tagged buffers (their layout never depends on T)
 constexpr int kMaxEPW = 4;             // router experts per workgroup
 constexpr long long kTimeoutTicks = 400000000LL;   // 4 s of the 100 MHz wall clock
+constexpr int kHBW = 32;               // words per (pair, 16-row chunk) h line (8 hi pairs, 8 lo pairs)
 constexpr int kSLW = 32;               // tagged words per (workgroup, token) residual line
 constexpr int kSSWord = 16;            // word of that line holding the sum of squares (2 words)
 constexpr int kLGW = 8;                // tagged words per (workgroup, token) logit line
-constexpr int kFLW = 8;                // words per workgroup flag (64 B apart)
-constexpr int kHBW = 32;               // words per (pair, 16-row chunk) h line (8 hi pairs, 8 lo pairs)
+constexpr int kFLW = 16;               // words per workgroup flag: one 128-byte line each
 constexpr int kMaxItemsInFlight = 2;   // gate/up items whose loads are issued together
 constexpr int kXhWords = 36;           // words per u block row in LDS: 16 hi pairs, 16 lo pairs, 4 pad
 constexpr int kMaxDPW = 16;            // d_model rows per workgroup
@@ -42,15 +42,11 @@ struct StackParams {
     double eps;
     int G;
     uint32_t* hdr;      // workspace header (see kHdr*)
-    u64* sl;            // [G][T][kSLW]  residual rows of workgroup g (+ sum of squares), tagged
-    u64* lg;            // [G][T][kLGW]  fp64 logits of workgroup g's experts (lo, hi words), tagged
-    u64* fl;            // [G][kFLW]     flag: workgroup g's SwiGLU rows of this layer are stored
+    u64* sl;            // [G][kSlots][kSLW]  residual rows of workgroup g (+ sum of squares), tagged
+    u64* lg;            // [G][kSlots][kLGW]  fp64 logits of workgroup g's experts (lo, hi words), tagged
+    u64* fl;            // [G][kFLW]          flag: workgroup g's SwiGLU rows of this layer are stored
     uint32_t* hp;       // [L][T*K][F/16][kHBW] SwiGLU h as fp16 pairs: 8 hi words, then 8 lo words
-    int lds_us, lds_part, lds_misc, lds_pre, lds_wr, lds_xh;
-    // down-projection rows prefetched into LDS: up to pre_cap distinct
-    // experts, each [rows][blocks][W] codes (pre_cstride bytes) followed by
-    // [rows][blocks] fp16 scales (pre_sstride bytes); copy granules in bytes
-    int pre_cap, pre_cstride, pre_sstride, pre_cgran, pre_sgran;
+    int lds_us, lds_part, lds_misc, lds_wr, lds_xh;
 };
 
 __host__ __device__ inline int misc_head_bytes(int PT, int T) { return (16 * PT + 2 * PT * T + 15) & ~15; }

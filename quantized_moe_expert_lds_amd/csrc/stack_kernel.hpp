@@ -35,6 +35,10 @@
 // (payload + epoch, one agent-scope atomic each; see ll_store): a reader
 // spins on exactly the words it needs until they carry this layer's epoch,
 // so no grid-wide barrier is needed and the data arrive with the signal.
+// Every 128-byte line of these buffers has a single writer workgroup.
+// Lines shared by words of several writers (workgroups on different XCDs)
+// returned wrong logits in tests, without any wait timing out, while the
+// same exchange over single-writer lines was exact.
 // The SwiGLU rows (many words read by every workgroup) are stored once per
 // layer and launch with write-through agent-scope stores into a buffer of
 // their own per layer, followed by the writer's tagged flag; readers load
@@ -60,38 +64,6 @@ using namespace qmoe_dev;
 using namespace qmoe::stk;
 
 constexpr int kMaxDevices = 64;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One direct-to-LDS chunk: lane i copies GRAN bytes from src + off + i*GRAN
-// to dst + off + i*GRAN (LDS address = M0 base + lane id * GRAN); lanes past
-// `bytes` are masked off.  The data is in LDS once the issuing wave has
-// waited for vmcnt(0).
-__device__ __forceinline__ void dma_chunk(const char* src, char* dst, int off, int bytes, int gran) {
-    const int lane = threadIdx.x & 63;
-    if (gran == 16) {
-        if (off + lane * 16 < bytes)
-            __builtin_amdgcn_global_load_lds(src + off + lane * 16, (lds_void_t*)(dst + off), 16, 0, 0);
-    } else {
-        if (off + lane * 4 < bytes)
-            __builtin_amdgcn_global_load_lds(src + off + lane * 4, (lds_void_t*)(dst + off), 4, 0, 0);
-    }
-}
-
-// Copy `bytes` (a multiple of 16, 16-byte aligned) to LDS, 1 KB chunks spread
-// over waves w0 .. w0+nw-1.
-__device__ __forceinline__ void dma_to_lds(const void* src, void* dst, int bytes, int w0, int nw) {
-    const int wave = (threadIdx.x >> 6) - w0;
-    for (int off = wave * 1024; off < bytes; off += nw * 1024)
-        dma_chunk((const char*)src, (char*)dst, off, bytes, 16);
-}
-
-struct LdsCopy {
-    const void* src;
-    void* dst;
-    int bytes;
-};
-
 
 // ------------------------------------------------------- coherent stores
 __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
@@ -248,6 +220,94 @@ __device__ void wave_topk_core(const double* z, int e_lo, int e_hi, int K, doubl
     }
 }
 
+// Top-k of z[0..E) (E <= 64 * kPer) by one wavefront, exact, ranked by
+// (z desc, id asc) and written in rank order to out_v / out_i.  With m the
+// largest logit, logit v falls in bin floor((m - v) * kBinScale), or kBins
+// when it lies farther than the range.  Rounding is monotone, so the K-th
+// largest value tau has the smallest bin b* whose cumulative count reaches
+// K: every logit >= tau lies in a bin <= b*, every logit in a bin < b* is
+// larger than tau.  b* comes from a binary search over the bins whose counts
+// are ballots (no LDS, no atomics); the C logits in bins <= b* are compacted
+// into LDS and each is ranked against all C by broadcast reads.  Returns
+// false, with nothing written, when fewer than K logits lie in range or more
+// than 64 are candidates (clustered logits); the caller then takes the
+// round-by-round selection.  cand_v / cand_i: 64 entries, private to the wave.
+constexpr int kBins = 1024;
+constexpr double kBinScale = 64.0;
+
+template <int kPer>
+__device__ bool wave_topk_bins(const double* z, int E, int K, double* out_v, int* out_i, double* cand_v,
+                               int* cand_i) {
+    const int lane = threadIdx.x & 63;
+    double v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? z[e] + 0.0 : -INFINITY;
+    }
+    double mx = v[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) mx = fmax(mx, v[i]);
+    const double m = wave_max_f64(mx);
+    int bin[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const double dd = (m - v[i]) * kBinScale;
+        bin[i] = dd < (double)kBins ? (int)dd : kBins;
+    }
+    auto count_le = [&](int b) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) c += __popcll(__ballot(bin[i] <= b));
+        return c;
+    };
+    if (count_le(kBins - 1) < K) return false;
+    int lo = 0, hi = kBins - 1;                       // b* lies in [lo, hi]
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (count_le(mid) >= K) hi = mid;
+        else lo = mid + 1;
+    }
+    // compaction: slot i's candidates follow those of slots < i, in lane order
+    int C = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const bool c = bin[i] <= lo;
+        const unsigned long long bal = __ballot(c);
+        const int p = C + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+        if (c && p < 64) {
+            cand_v[p] = v[i];
+            cand_i[p] = lane + 64 * i;
+        }
+        C += __popcll(bal);
+    }
+    if (C > 64) return false;
+    const int C4 = (C + 3) & ~3;
+    if (lane >= C && lane < C4) {                     // sentinels rank after every candidate
+        cand_v[lane] = -INFINITY;
+        cand_i[lane] = 0x7fffffff;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int me = lane < C ? lane : 0;
+    const double cv = cand_v[me];
+    const int ci = cand_i[me];
+    int rank = 0;
+    for (int q = 0; q < C4; q += 4) {
+        const double2 a = *reinterpret_cast<const double2*>(cand_v + q);
+        const double2 b = *reinterpret_cast<const double2*>(cand_v + q + 2);
+        const int4 ii = *reinterpret_cast<const int4*>(cand_i + q);
+        rank += ((a.x > cv) || (a.x == cv && ii.x < ci)) + ((a.y > cv) || (a.y == cv && ii.y < ci)) +
+                ((b.x > cv) || (b.x == cv && ii.z < ci)) + ((b.y > cv) || (b.y == cv && ii.w < ci));
+    }
+    if (lane < C && rank < K) {
+        out_v[rank] = cv;
+        out_i[rank] = ci;
+    }
+    __builtin_amdgcn_wave_barrier();
+    return true;
+}
+
 // softmax gates over K sorted logits (LDS, rank order)
 __device__ __forceinline__ void wave_gates(const double* sv, const int* si, int K, int* ids, float* gates) {
     const int lane = threadIdx.x & 63;
@@ -333,6 +393,7 @@ __device__ __forceinline__ bool ll_wait(Addr addr, Tag tg, uint32_t (&out)[N], i
         int it = 0;
         while (pend) {
             if ((++it & 15) == 0 && stack_should_stop(P, t0)) return false;
+            __builtin_amdgcn_s_sleep(2);
 #pragma unroll
             for (int i = 0; i < N; ++i)
                 if ((pend >> i) & 1) v[i] = ll_load(addr(i));
@@ -511,7 +572,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     float* part = reinterpret_cast<float*>(lds + P.lds_part);             // [PT][DPW][nkbF]
     double* s_z = reinterpret_cast<double*>(lds + P.lds_part);            // [T][E] (dead before part is used)
     float* s_z_f = reinterpret_cast<float*>(lds + P.lds_us);              // [PT][DPW] per-pair sums in DOWN
-    uint32_t* pre = reinterpret_cast<uint32_t*>(lds + P.lds_pre);         // prefetched down blocks
     unsigned char* misc = lds + P.lds_misc;
     int* s_ids = reinterpret_cast<int*>(misc);                            // [PT]
     float* s_gates = reinterpret_cast<float*>(s_ids + PT);                // [PT]
@@ -527,6 +587,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     double* s_cand_v = reinterpret_cast<double*>(misc + misc_tail_offset(PT, T, DPW));   // [256] top-k lists
     int* s_cand_i = reinterpret_cast<int*>(s_cand_v + 256);               // [256]
     unsigned* s_cand_k = reinterpret_cast<unsigned*>(s_cand_i + 256);     // [256]
+    double* s_sel_v = reinterpret_cast<double*>(s_cand_k + 256);          // [256] selected, rank order
+    int* s_sel_i = reinterpret_cast<int*>(s_sel_v + 256);                 // [256]
 
     const size_t hp_layer = (size_t)PT * nch * kHBW;
 
@@ -535,17 +597,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
 #pragma unroll
     for (int t = 0; t < T; ++t) base[t] = P.hdr[kHdrBase + t];
 
-    // router rows of this workgroup's experts live in LDS, copied by DMA one
-    // layer ahead (expert-major rows are contiguous)
+    // router rows of this workgroup's experts live in LDS; the next layer's
+    // are loaded into registers while the workgroup waits for the SwiGLU
+    // flags and stored after the wait
     float* wr_lds = reinterpret_cast<float*>(lds + P.lds_wr);             // [EPW][D]
     const int e_first = w * EPW;
     const int my_experts = max(0, min(EPW, E - e_first));
-    auto router_copy = [&](int layer) {
-        return LdsCopy{m.router_w + ((size_t)layer * E + e_first) * D, wr_lds, my_experts * D * 4};
+    constexpr int kRW = (EPWM * kStackMaxD / 4 + kThreads - 1) / kThreads;   // float4 per thread
+    const int rw_n4 = my_experts * D / 4;
+    auto load_router = [&](int layer, float4 (&rv)[kRW]) {
+        const float4* src = reinterpret_cast<const float4*>(m.router_w + ((size_t)layer * E + e_first) * D);
+#pragma unroll
+        for (int i = 0; i < kRW; ++i) {
+            const int f = tid + i * kThreads;
+            rv[i] = f < rw_n4 ? src[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     };
-    if (my_experts > 0) {
-        const LdsCopy c = router_copy(0);
-        dma_to_lds(c.src, c.dst, c.bytes, 0, 4);
+    auto store_router = [&](const float4 (&rv)[kRW]) {
+#pragma unroll
+        for (int i = 0; i < kRW; ++i) {
+            const int f = tid + i * kThreads;
+            if (f < rw_n4) reinterpret_cast<float4*>(wr_lds)[f] = rv[i];
+        }
+    };
+    {
+        float4 rv[kRW];
+        load_router(0, rv);
+        store_router(rv);
     }
     if (tid == 0) s_misc[1] = 0;
     for (int i = tid; i < T * nrows; i += kThreads) {
@@ -568,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             // for them (x, or the residual rows the workgroups published),
             // forms u, stores u's fp16 halves for the expert phase and
             // accumulates its share of this workgroup's logits.
-            constexpr int KR = T >= 8 ? 2 : (T >= 4 ? 4 : 8);   // elements per token per round of waits
+            constexpr int KR = T >= 5 ? 2 : (T >= 3 ? 4 : 8);   // elements per token per round of waits
             float hv[KR][T];
             bool ok = true;
             // tagged words of the residual rows (written by layer l - 1)
@@ -734,57 +812,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
             STACK_CHECK_OK(ok);
         }
-        constexpr bool kSplitTopk = T == 1 && KPER >= 4;
-        const bool split_topk = kSplitTopk && 4 * K <= 64;
-        if (split_topk) {
-            // batch 1: each wave selects the top K of a quarter of the
-            // experts, then wave 0 merges the 4 K candidates.  With one token
-            // the distinct experts are the selected ones in rank order; the
-            // gates are formed later, while the expert weight loads are in
-            // flight.
-            constexpr int kq = KPER >= 4 ? KPER / 4 : 1;
-            wave_topk_core<kq>(s_z, 64 * kq * wave, min(E, 64 * kq * (wave + 1)), K, s_cand_v + wave * K,
-                               s_cand_i + wave * K, s_cand_k + wave * K);
-            __syncthreads();
-            if (wave == 0) {
-                wave_merge_topk(s_cand_v, s_cand_i, s_cand_k, 4 * K, K, s_cand_v + 64, s_cand_i + 64);
-                if (lane < K) {
-                    const int e = s_cand_i[64 + lane];
-                    s_ids[lane] = e;
-                    s_uniq[lane] = e;
-                    s_upair[lane] = (short)lane;
-                }
-                if (lane == 0) s_misc[0] = K;
-            }
-        } else {
-            for (int t = wave; t < T; t += 4) {
-                double* ov = s_cand_v + 64 * wave;
-                int* oi = s_cand_i + 64 * wave;
+        // top-k and gates per token, one wave per token: the binned
+        // selection, or the round-by-round one when it declines
+        for (int t = wave; t < T; t += 4) {
+            double* ov = s_sel_v + 64 * wave;
+            int* oi = s_sel_i + 64 * wave;
+            if (!wave_topk_bins<KPER>(s_z + (size_t)t * E, E, K, ov, oi, s_cand_v + 64 * wave,
+                                      s_cand_i + 64 * wave))
                 wave_topk_core<KPER>(s_z + (size_t)t * E, 0, E, K, ov, oi, s_cand_k + 64 * wave);
-                wave_gates(ov, oi, K, s_ids + t * K, s_gates + t * K);
-            }
+            wave_gates(ov, oi, K, s_ids + t * K, s_gates + t * K);
         }
         __syncthreads();
-        // gates of the batch-1 path (wave 0), and the routing outputs
-        auto finish_gates = [&]() {
-            if constexpr (kSplitTopk) {
-                wave_gates(s_cand_v + 64, s_cand_i + 64, K, s_ids, s_gates);
-                if (w == 0 && P.ids_out && lane < K) {
-                    P.ids_out[(size_t)l * PT + lane] = s_cand_i[64 + lane];
-                    P.gates_out[(size_t)l * PT + lane] = s_gates[lane];
-                }
-            }
-        };
-        bool gates_pending = split_topk;
-        if (!split_topk && w == 0 && P.ids_out) {
+        if (w == 0 && P.ids_out) {
             for (int i = tid; i < PT; i += kThreads) {
                 P.ids_out[(size_t)l * PT + i] = s_ids[i];
                 P.gates_out[(size_t)l * PT + i] = s_gates[i];
             }
         }
         // distinct experts of the batch, in slot order of first appearance
-        if (split_topk) {
-            // set above
+        if (T == 1) {
+            // one token: the distinct experts are its selected ones, in rank order
+            if (tid < K) {
+                s_uniq[tid] = s_ids[tid];
+                s_upair[tid] = (short)tid;
+            }
+            if (tid == 0) s_misc[0] = K;
         } else if (PT <= 64) {
             if (wave == 0) {
                 // lane p holds pair p; its expert's first pair is the lowest q
@@ -834,35 +886,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         const int U = s_misc[0];
 
         const size_t lstrideD = (size_t)E * D * nkbF;
-        const int uid = lane < U ? s_uniq[lane] : 0;     // distinct expert `lane` (first 64)
-        const int n_pre = min(U, P.pre_cap);
-        // copy this workgroup's down-projection rows d_lo .. d_hi of the first
-        // n_pre distinct experts (and the next layer's router rows) into LDS.
-        // Waves 1-3 issue the copies while wave 0 waits for the other
-        // workgroups' SwiGLU flags; chunks are dealt to the three waves
-        // round-robin.  Wave-uniform control flow only: every lane of the
-        // wave takes part in a chunk.
-        auto issue_down_prefetch = [&]() {
-            if (l + 1 < L && my_experts > 0) {
-                const LdsCopy c = router_copy(l + 1);
-                dma_to_lds(c.src, c.dst, c.bytes, 1, 3);
-            }
-            if (nrows <= 0) return;
-            const int cbytes = nrows * nkbF * W * 4, sbytes = nrows * nkbF * 2;
-            int ci = 0;
-            for (int u = 0; u < n_pre; ++u) {
-                const int e = u < 64 ? __builtin_amdgcn_readlane(uid, u) : s_uniq[u];
-                const size_t row0 = ((size_t)l * E + e) * D + d_lo;
-                const char* csrc = reinterpret_cast<const char*>(m.down_q + row0 * nkbF * W);
-                const char* ssrc = reinterpret_cast<const char*>(m.down_s + row0 * nkbF);
-                char* cdst = reinterpret_cast<char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
-                for (int off = 0; off < cbytes; off += 64 * P.pre_cgran, ++ci)
-                    if (ci % 3 == wave - 1) dma_chunk(csrc, cdst, off, cbytes, P.pre_cgran);
-                for (int off = 0; off < sbytes; off += 64 * P.pre_sgran, ++ci)
-                    if (ci % 3 == wave - 1) dma_chunk(ssrc, cdst + P.pre_cstride, off, sbytes, P.pre_sgran);
-            }
-        };
-
         {
             const int n_items = U * nch;
             const size_t lstrideGU = (size_t)E * F * nkbD;
@@ -898,10 +921,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         load_block<W>(r < 4 ? m.gate_q : m.up_q, blk, q[a][r]);
                         sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
                     }
-                }
-                if (gates_pending) {
-                    gates_pending = false;
-                    if (wave == 0) finish_gates();
                 }
                 // Gate and up sums of (item a, token t, row r) are formed one
                 // token at a time by the same instruction sequence for every
@@ -981,7 +1000,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 __syncthreads();
             }
         }
-        if (gates_pending && wave == 0) finish_gates();   // workgroups without gate/up items
         // this workgroup's SwiGLU rows of layer l are stored (every thread's
         // write-through stores have completed): raise its flag
         __builtin_amdgcn_s_waitcnt(0);
@@ -990,32 +1008,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
 
         // -------------------------------------------------------------- DOWN
         {
-            // wave 0 waits for every workgroup's flag while waves 1-3 copy the
-            // down rows (and the next router rows) into LDS
-            bool ok = true;
-            if (wave == 0) {
-                for (int g0 = 0; g0 < G; g0 += 4 * 64) {
-                    uint32_t pay[4];
-                    ok = ok && ll_wait<4>(
-                        [&](int i) -> const u64* { return P.fl + (size_t)min(g0 + lane + 64 * i, G - 1) * kFLW; },
-                        [&](int i) { return base[0] + (uint32_t)l + 1u; }, pay, 4, P);
+            // before waiting for the flags, issue the loads the phase needs
+            // anyway: the next layer's router rows and the down rows of this
+            // thread's first (expert, block) item; they land during the wait
+            float4 rv[kRW];
+            if (l + 1 < L) load_router(l + 1, rv);
+            uint32_t qd0[8][W];
+            float scd0[8];
+            if (tid < U * nkbF && nrows > 0) {
+                const int u = tid / nkbF, kb = tid - u * nkbF;
+                const int e = s_uniq[u];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int rr = min(r, nrows - 1);
+                    const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + rr) * nkbF + kb;
+                    load_block<W>(m.down_q, blk, qd0[r]);
+                    scd0[r] = h2f(m.down_s[blk]);
                 }
-            } else {
-                issue_down_prefetch();
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            // every workgroup's flag: thread g waits for workgroup g's
+            bool ok = true;
+            for (int g = tid; g < G; g += kThreads) {
+                uint32_t pay[1];
+                ok = ok && ll_wait<1>([&](int) -> const u64* { return P.fl + (size_t)g * kFLW; },
+                                      [&](int) { return base[0] + (uint32_t)l + 1u; }, pay, 1, P);
+            }
             STACK_CHECK_OK(ok);
-        }
-        {
+            if (l + 1 < L) store_router(rv);
             const uint32_t* hpp = P.hp + (size_t)l * hp_layer;
             constexpr int kTG = T <= 2 ? T : 2;     // tokens whose h halves are held at once
             for (int it = tid; it < U * nkbF; it += kThreads) {
                 const int u = it / nkbF, kb = it - u * nkbF;
                 const int e = s_uniq[u];
-                const bool in_lds = u < n_pre;
-                const char* cb = reinterpret_cast<const char*>(pre) + (size_t)u * (P.pre_cstride + P.pre_sstride);
-                const uint32_t* cw = reinterpret_cast<const uint32_t*>(cb);
-                const uint16_t* sw = reinterpret_cast<const uint16_t*>(cb + P.pre_cstride);
+#pragma unroll 1
                 for (int t0 = 0; t0 < T; t0 += kTG) {
                     int prs[kTG];
                     bool any = false;
@@ -1047,16 +1072,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     for (int r0 = 0; r0 < nrows; r0 += 8) {
                         uint32_t qd[8][W];
                         float scd[8];
+                        if (it == tid && r0 == 0) {
+                            // the rows loaded before the wait
 #pragma unroll
-                        for (int r = 0; r < 8; ++r) {
-                            // rows from LDS when prefetched (nrows <= 8 then), else
-                            // clamped rows from memory: every load is issued
-                            const int rr = min(r0 + r, nrows - 1);
-                            if (in_lds) {
+                            for (int r = 0; r < 8; ++r) {
 #pragma unroll
-                                for (int k = 0; k < W; ++k) qd[r][k] = cw[(rr * nkbF + kb) * W + k];
-                                scd[r] = h2f(sw[rr * nkbF + kb]);
-                            } else {
+                                for (int k = 0; k < W; ++k) qd[r][k] = qd0[r][k];
+                                scd[r] = scd0[r];
+                            }
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 8; ++r) {  // clamped rows: every load is issued
+                                const int rr = min(r0 + r, nrows - 1);
                                 const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + rr) * nkbF + kb;
                                 load_block<W>(m.down_q, blk, qd[r]);
                                 scd[r] = h2f(m.down_s[blk]);
