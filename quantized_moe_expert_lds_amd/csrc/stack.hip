@@ -33,13 +33,12 @@ StackWs stack_ws_layout(int T, int D, int F, int E, int K, int G, int L) {
 
 // LDS plan of one workgroup.
 struct StackLds {
-    size_t us, part, wr, xh, misc, total;
+    size_t us, part, xh, misc, total;
 };
 
 static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bits) {
     StackLds p{};
     const int DPW = (D + G - 1) / G;
-    const int EPW = (E + G - 1) / G;
     const int PT = T * K;
     const int nkbF = F / 32;
     (void)bits;
@@ -54,12 +53,8 @@ static StackLds stack_lds_plan(int T, int D, int F, int E, int K, int G, int bit
     const size_t xh_bytes = sizeof(uint32_t) * (size_t)T * (D / 32) * kXhWords;
     p.xh = off + z_bytes;
     off += align256(part_bytes > z_bytes + xh_bytes ? part_bytes : z_bytes + xh_bytes);
-    p.wr = off;                        // router rows
-    off += align256(sizeof(float) * (size_t)EPW * D);
     p.misc = off;
-    // top-k scratch: candidates (value, id, key) and selections (value, id),
-    // 64 per wave
-    off += align256((size_t)misc_tail_offset(PT, T, DPW) + 256 * (2 * sizeof(double) + 3 * sizeof(int)));
+    off += align256((size_t)misc_tail_offset(PT, T, DPW) + kTopkScratchBytes);
     p.total = off;
     return p;
 }
@@ -90,7 +85,6 @@ hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, 
     const StackLds pl = stack_lds_plan(T, m.d_model, m.d_ff, m.n_experts, m.top_k, G, m.bits);
     P.lds_us = (int)pl.us;
     P.lds_part = (int)pl.part;
-    P.lds_wr = (int)pl.wr;
     P.lds_xh = (int)pl.xh;
     P.lds_misc = (int)pl.misc;
     const size_t lds = pl.total;

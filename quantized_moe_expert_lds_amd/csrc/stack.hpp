@@ -23,6 +23,10 @@ constexpr int kFLW = 16;               // words per workgroup flag: one 128-byte
 constexpr int kMaxItemsInFlight = 2;   // gate/up items whose loads are issued together
 constexpr int kXhWords = 36;           // words per u block row in LDS: 16 hi pairs, 16 lo pairs, 4 pad
 constexpr int kMaxDPW = 16;            // d_model rows per workgroup
+// bytes of the per-wave top-k scratch at the end of the misc area:
+// candidates (value, id) 128 per wave, keys 64, selections (value, id) 64,
+// histogram 128
+constexpr int kTopkScratchBytes = 4 * (128 * (8 + 4) + 64 * 4 + 64 * (8 + 4) + 128 * 4);
 // workspace header (uint32 words): epoch bases of the 8 token slots, the
 // launch-completion counter and the error word
 constexpr int kHdrBase = 0;
@@ -46,7 +50,7 @@ struct StackParams {
     u64* lg;            // [G][kSlots][kLGW]  fp64 logits of workgroup g's experts (lo, hi words), tagged
     u64* fl;            // [G][kFLW]          flag: workgroup g's SwiGLU rows of this layer are stored
     uint32_t* hp;       // [L][T*K][F/16][kHBW] SwiGLU h as fp16 pairs: 8 hi words, then 8 lo words
-    int lds_us, lds_part, lds_misc, lds_wr, lds_xh;
+    int lds_us, lds_part, lds_misc, lds_xh;
 };
 
 __host__ __device__ inline int misc_head_bytes(int PT, int T) { return (16 * PT + 2 * PT * T + 15) & ~15; }

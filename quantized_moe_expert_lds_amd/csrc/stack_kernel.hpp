@@ -220,30 +220,52 @@ __device__ void wave_topk_core(const double* z, int e_lo, int e_hi, int K, doubl
     }
 }
 
+// Inclusive prefix sum over the 64 lanes (row_shr 1, 2, 4, 8 inside each
+// row of 16 lanes, then row_bcast 15 and 31 carry the row totals across).
+__device__ __forceinline__ int wave_scan_add(int v) {
+    v += dpp0<0x111, 0xf>(v);
+    v += dpp0<0x112, 0xf>(v);
+    v += dpp0<0x114, 0xf>(v);
+    v += dpp0<0x118, 0xf>(v);
+    v += dpp0<0x142, 0xa>(v);
+    v += dpp0<0x143, 0xc>(v);
+    return v;
+}
+
 // Top-k of z[0..E) (E <= 64 * kPer) by one wavefront, exact, ranked by
 // (z desc, id asc) and written in rank order to out_v / out_i.  With m the
-// largest logit, logit v falls in bin floor((m - v) * kBinScale), or kBins
-// when it lies farther than the range.  Rounding is monotone, so the K-th
-// largest value tau has the smallest bin b* whose cumulative count reaches
-// K: every logit >= tau lies in a bin <= b*, every logit in a bin < b* is
-// larger than tau.  b* comes from a binary search over the bins whose counts
-// are ballots (no LDS, no atomics); the C logits in bins <= b* are compacted
-// into LDS and each is ranked against all C by broadcast reads.  Returns
-// false, with nothing written, when fewer than K logits lie in range or more
-// than 64 are candidates (clustered logits); the caller then takes the
-// round-by-round selection.  cand_v / cand_i: 64 entries, private to the wave.
-constexpr int kBins = 1024;
-constexpr double kBinScale = 64.0;
+// largest logit, logit v falls in bin floor((m - v) * kHistScale), or in the
+// overflow bin kHistBins when it lies farther than the range.  Rounding is
+// monotone, so the K-th largest value tau lies in the first bin b* whose
+// cumulative count reaches K: every logit >= tau lies in a bin <= b*, every
+// logit in a bin < b* is larger than tau.  The histogram is built with LDS
+// adds, its prefix sum with DPP, b* with one ballot; the C logits in bins
+// <= b* are compacted into LDS (ballot + mbcnt; lanes with nothing to write
+// store to a discard area instead of branching) and each is ranked against
+// all C by broadcast reads, issued together for up to 16 candidates.  One
+// wave runs this straight-line code, so its time is the length of its
+// dependency chain, LDS round trips above all (VALU-to-scalar hand-offs cost
+// about as much: a ballot-count binary search over the bins measured
+// slower).  Returns false, with nothing written, when fewer than K logits
+// lie in range or more than 64 are candidates (clustered logits); the
+// caller then takes the round-by-round selection.  LDS private to the wave:
+// hist[kHistBins + 1] (128 reserved), cand_v / cand_i[128] (64 candidates,
+// then the discard area).
+constexpr int kHistBins = 64;
+constexpr double kHistScale = 16.0;
 
 template <int kPer>
-__device__ bool wave_topk_bins(const double* z, int E, int K, double* out_v, int* out_i, double* cand_v,
-                               int* cand_i) {
+__device__ bool wave_topk_hist(const double* z, int E, int K, double* out_v, int* out_i, int* hist,
+                               double* cand_v, int* cand_i) {
     const int lane = threadIdx.x & 63;
+    hist[lane] = 0;
+    hist[64 + lane] = 0;
     double v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? z[e] + 0.0 : -INFINITY;
+        const double x = z[min(e, E - 1)];
+        v[i] = e < E ? x + 0.0 : -INFINITY;
     }
     double mx = v[0];
 #pragma unroll
@@ -252,53 +274,59 @@ __device__ bool wave_topk_bins(const double* z, int E, int K, double* out_v, int
     int bin[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const double dd = (m - v[i]) * kBinScale;
-        bin[i] = dd < (double)kBins ? (int)dd : kBins;
+        const double dd = (m - v[i]) * kHistScale;
+        bin[i] = dd < (double)kHistBins ? (int)dd : kHistBins;
     }
-    auto count_le = [&](int b) {
-        int c = 0;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) c += __popcll(__ballot(bin[i] <= b));
-        return c;
-    };
-    if (count_le(kBins - 1) < K) return false;
-    int lo = 0, hi = kBins - 1;                       // b* lies in [lo, hi]
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (count_le(mid) >= K) hi = mid;
-        else lo = mid + 1;
-    }
-    // compaction: slot i's candidates follow those of slots < i, in lane order
-    int C = 0;
+    for (int i = 0; i < kPer; ++i) atomicAdd(&hist[bin[i]], 1);
+    __builtin_amdgcn_wave_barrier();
+    const int c = wave_scan_add(hist[lane]);
+    const unsigned long long reach = __ballot(c >= K);
+    if (!reach) return false;
+    const int bstar = __ffsll((unsigned long long)reach) - 1;
+    const int C = __builtin_amdgcn_readlane(c, bstar);
+    if (C > 64) return false;
+    int base = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const bool c = bin[i] <= lo;
-        const unsigned long long bal = __ballot(c);
-        const int p = C + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-        if (c && p < 64) {
-            cand_v[p] = v[i];
-            cand_i[p] = lane + 64 * i;
-        }
-        C += __popcll(bal);
+        const bool cnd = bin[i] <= bstar;
+        const unsigned long long bal = __ballot(cnd);
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+        const int p = cnd ? pos : 64 + lane;
+        cand_v[p] = v[i];
+        cand_i[p] = lane + 64 * i;
+        base += __popcll(bal);
     }
-    if (C > 64) return false;
     const int C4 = (C + 3) & ~3;
-    if (lane >= C && lane < C4) {                     // sentinels rank after every candidate
-        cand_v[lane] = -INFINITY;
-        cand_i[lane] = 0x7fffffff;
+    {
+        const int p = lane >= C && lane < C4 ? lane : 64 + lane;   // sentinels rank after every candidate
+        cand_v[p] = -INFINITY;
+        cand_i[p] = 0x7fffffff;
     }
     __builtin_amdgcn_wave_barrier();
     const int me = lane < C ? lane : 0;
     const double cv = cand_v[me];
     const int ci = cand_i[me];
-    int rank = 0;
-    for (int q = 0; q < C4; q += 4) {
+    auto before4 = [&](int q) {
         const double2 a = *reinterpret_cast<const double2*>(cand_v + q);
         const double2 b = *reinterpret_cast<const double2*>(cand_v + q + 2);
         const int4 ii = *reinterpret_cast<const int4*>(cand_i + q);
-        rank += ((a.x > cv) || (a.x == cv && ii.x < ci)) + ((a.y > cv) || (a.y == cv && ii.y < ci)) +
-                ((b.x > cv) || (b.x == cv && ii.z < ci)) + ((b.y > cv) || (b.y == cv && ii.w < ci));
+        return ((a.x > cv) || (a.x == cv && ii.x < ci)) + ((a.y > cv) || (a.y == cv && ii.y < ci)) +
+               ((b.x > cv) || (b.x == cv && ii.z < ci)) + ((b.y > cv) || (b.y == cv && ii.w < ci));
+    };
+    int rank = 0;
+    if (C4 <= 16) {
+        // the reads of the first 16 entries are issued together; entries
+        // past C4 hold stale data and are left out
+        int r4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r4[j] = before4(4 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rank += 4 * j < C4 ? r4[j] : 0;
+    } else {
+        for (int q = 0; q < C4; q += 4) rank += before4(q);
     }
     if (lane < C && rank < K) {
         out_v[rank] = cv;
@@ -350,6 +378,19 @@ __device__ void wave_merge_topk(const double* cv, const int* ci, const unsigned*
         out_v[rank] = v;
         out_i[rank] = id;
     }
+}
+
+// Workgroup barrier that orders LDS only.  Outstanding global loads and
+// stores stay in flight: __syncthreads() also waits for every one of them,
+// and a write-through store is acknowledged only after a round trip to
+// memory, which put that latency on every barrier that followed a
+// hand-over store.  Global data is never shared between the threads of a
+// workgroup except through the SwiGLU-row protocol, which waits for its
+// stores explicitly.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ------------------------------------------------------ tagged exchanges
@@ -414,7 +455,7 @@ __device__ __forceinline__ bool ll_wait(Addr addr, Tag tg, uint32_t (&out)[N], i
 #define STACK_CHECK_OK(ok)                                                                           \
     do {                                                                                             \
         if (!(ok)) s_misc[1] = 1;                                                                    \
-        __syncthreads();                                                                             \
+        lds_barrier();                                                                               \
         if (s_misc[1]) {                                                                             \
             if (threadIdx.x == 0)                                                                    \
                 __hip_atomic_store(&P.hdr[kHdrErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
@@ -584,11 +625,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     double* s_r = reinterpret_cast<double*>(s_misc + 4);                  // [4][T] per-wave sums of squares
     float* s_hres = reinterpret_cast<float*>(s_r + 4 * T);                // [T][DPW] own residual rows
     float* s_gu = s_hres + T * DPW;                                       // see gu_floats
-    double* s_cand_v = reinterpret_cast<double*>(misc + misc_tail_offset(PT, T, DPW));   // [256] top-k lists
-    int* s_cand_i = reinterpret_cast<int*>(s_cand_v + 256);               // [256]
-    unsigned* s_cand_k = reinterpret_cast<unsigned*>(s_cand_i + 256);     // [256]
-    double* s_sel_v = reinterpret_cast<double*>(s_cand_k + 256);          // [256] selected, rank order
-    int* s_sel_i = reinterpret_cast<int*>(s_sel_v + 256);                 // [256]
+    double* s_cand_v = reinterpret_cast<double*>(misc + misc_tail_offset(PT, T, DPW));   // [4][128] top-k candidates
+    int* s_cand_i = reinterpret_cast<int*>(s_cand_v + 512);               // [4][128]
+    unsigned* s_cand_k = reinterpret_cast<unsigned*>(s_cand_i + 512);     // [4][64]
+    double* s_sel_v = reinterpret_cast<double*>(s_cand_k + 256);          // [4][64] selected, rank order
+    int* s_sel_i = reinterpret_cast<int*>(s_sel_v + 256);                 // [4][64]
+    int* s_hist = s_sel_i + 256;                                          // [4][128]
 
     const size_t hp_layer = (size_t)PT * nch * kHBW;
 
@@ -597,34 +639,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
 #pragma unroll
     for (int t = 0; t < T; ++t) base[t] = P.hdr[kHdrBase + t];
 
-    // router rows of this workgroup's experts live in LDS; the next layer's
-    // are loaded into registers while the workgroup waits for the SwiGLU
-    // flags and stored after the wait
-    float* wr_lds = reinterpret_cast<float*>(lds + P.lds_wr);             // [EPW][D]
+    // router rows of this workgroup's experts: each thread multiplies only
+    // the elements d = tid + 256 k of them, which it loads into registers at
+    // the start of the layer's ROUTE phase, ahead of its waits
     const int e_first = w * EPW;
     const int my_experts = max(0, min(EPW, E - e_first));
-    constexpr int kRW = (EPWM * kStackMaxD / 4 + kThreads - 1) / kThreads;   // float4 per thread
-    const int rw_n4 = my_experts * D / 4;
-    auto load_router = [&](int layer, float4 (&rv)[kRW]) {
-        const float4* src = reinterpret_cast<const float4*>(m.router_w + ((size_t)layer * E + e_first) * D);
-#pragma unroll
-        for (int i = 0; i < kRW; ++i) {
-            const int f = tid + i * kThreads;
-            rv[i] = f < rw_n4 ? src[f] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    auto store_router = [&](const float4 (&rv)[kRW]) {
-#pragma unroll
-        for (int i = 0; i < kRW; ++i) {
-            const int f = tid + i * kThreads;
-            if (f < rw_n4) reinterpret_cast<float4*>(wr_lds)[f] = rv[i];
-        }
-    };
-    {
-        float4 rv[kRW];
-        load_router(0, rv);
-        store_router(rv);
-    }
+    constexpr int kDK = kStackMaxD / kThreads;                            // d elements per thread
     if (tid == 0) s_misc[1] = 0;
     for (int i = tid; i < T * nrows; i += kThreads) {
         const int t = i / nrows, r = i - t * nrows;
@@ -640,6 +660,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         if (m.router_b && tid < EPWM * T) {
             const int j = tid / T, e = w * EPW + j;
             if (j < EPW && e < E) bias_v = m.router_b[(size_t)l * E + e];
+        }
+        // this thread's router elements, clamped in bounds (every load is
+        // issued, so later waits count them at compile time); loads return
+        // in order, so they arrive during the waits below
+        float wr[EPWM][kDK];
+        {
+            const float* rw = m.router_w + ((size_t)l * E + min(e_first, E - 1)) * D;
+#pragma unroll
+            for (int j = 0; j < EPWM; ++j)
+#pragma unroll
+                for (int k = 0; k < kDK; ++k)
+                    wr[j][k] = rw[(size_t)min(j, max(my_experts - 1, 0)) * D + min(tid + k * kThreads, D - 1)];
         }
         {
             // Thread tid owns elements d = tid + 256 k of every token: it waits
@@ -711,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     const double v = wave_sum_f64(ss[t]);
                     if (lane == 0) s_r[wave * T + t] = v;
                 }
-                __syncthreads();
+                lds_barrier();
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const double tot = ((s_r[t] + s_r[T + t]) + s_r[2 * T + t]) + s_r[3 * T + t];
@@ -726,7 +758,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             for (int j = 0; j < EPWM; ++j)
 #pragma unroll
                 for (int t = 0; t < T; ++t) acc[j][t] = 0.0;
-            for (int k0 = 0; k0 * kThreads < D; k0 += KR) {
+#pragma unroll
+            for (int k0 = 0; k0 < kDK; k0 += KR) {
+                if (k0 * kThreads >= D) break;
                 if (k0 > 0) {
                     if (l == 0) {
                         load_x(k0);
@@ -758,7 +792,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         xh[xi + 32] = ul;
 #pragma unroll
                         for (int j = 0; j < EPWM; ++j)
-                            if (j < my_experts) acc[j][t] = fma((double)uv, (double)wr_lds[j * D + d], acc[j][t]);
+                            if (j < my_experts) acc[j][t] = fma((double)uv, (double)wr[j][k0 + kr], acc[j][t]);
                     }
                 }
             }
@@ -771,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     if (lane == 0) s_red[(wave * EPWM + j) * T + t] = v;
                 }
             }
-            __syncthreads();
+            lds_barrier();
             if (tid < EPWM * T) {
                 const int j = tid / T, t = tid - j * T;
                 const int e = w * EPW + j;
@@ -812,17 +846,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
             STACK_CHECK_OK(ok);
         }
-        // top-k and gates per token, one wave per token: the binned
-        // selection, or the round-by-round one when it declines
+        // top-k and gates per token, one wave per token: the histogram
+        // selection, or the round-by-round one
         for (int t = wave; t < T; t += 4) {
             double* ov = s_sel_v + 64 * wave;
             int* oi = s_sel_i + 64 * wave;
-            if (!wave_topk_bins<KPER>(s_z + (size_t)t * E, E, K, ov, oi, s_cand_v + 64 * wave,
-                                      s_cand_i + 64 * wave))
+            // the histogram selection runs faster alone; with four waves
+            // at once their LDS adds collide and the rounds win
+            if (T > 2 || !wave_topk_hist<KPER>(s_z + (size_t)t * E, E, K, ov, oi, s_hist + 128 * wave,
+                                               s_cand_v + 128 * wave, s_cand_i + 128 * wave))
                 wave_topk_core<KPER>(s_z + (size_t)t * E, 0, E, K, ov, oi, s_cand_k + 64 * wave);
             wave_gates(ov, oi, K, s_ids + t * K, s_gates + t * K);
         }
-        __syncthreads();
+        lds_barrier();
         if (w == 0 && P.ids_out) {
             for (int i = tid; i < PT; i += kThreads) {
                 P.ids_out[(size_t)l * PT + i] = s_ids[i];
@@ -862,7 +898,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 for (int q = 0; q < p; ++q) first &= (s_ids[q] != e);
                 s_first[p] = first;
             }
-            __syncthreads();
+            lds_barrier();
             for (int p = tid; p < PT; p += kThreads) {
                 if (!s_first[p]) continue;
                 int idx = 0;
@@ -882,10 +918,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 s_misc[0] = U;
             }
         }
-        __syncthreads();
+        lds_barrier();
         const int U = s_misc[0];
 
         const size_t lstrideD = (size_t)E * D * nkbF;
+        // The down rows of this thread's first (expert, block) item, which
+        // the DOWN phase needs whatever the flags say, are loaded right after
+        // each batch of item loads and land during the SwiGLU dot products.
+        // Loads return in order: issued before the item loads they would hold
+        // up the item products, issued before the flag wait every poll of it.
+        uint32_t qd0[8][W];
+        uint16_t scd0[8];           // raw fp16 scales: converting them here would wait for the loads
+        auto issue_down_prefetch = [&]() {
+            // unconditional and clamped in bounds (only the rows of a real
+            // first item are used), so later waits count them at compile time
+            const int it = min(tid, U * nkbF - 1);
+            const int u = it / nkbF, kb = it - u * nkbF;
+            const int e = s_uniq[u];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int d = min(d_lo + min(r, nrows - 1), D - 1);
+                const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d) * nkbF + kb;
+                load_block<W>(m.down_q, blk, qd0[r]);
+                scd0[r] = m.down_s[blk];
+            }
+        };
         {
             const int n_items = U * nch;
             const size_t lstrideGU = (size_t)E * F * nkbD;
@@ -922,6 +979,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         sr[a][r] = (r < 4 ? m.gate_s : m.up_s)[blk];
                     }
                 }
+                issue_down_prefetch();       // the same rows every batch
                 // Gate and up sums of (item a, token t, row r) are formed one
                 // token at a time by the same instruction sequence for every
                 // batch size (the block products rounded on their own, never
@@ -980,7 +1038,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     const float hv = silu_mul(gv, uv);
                     if (a < kMaxItemsInFlight && ((tm >> t) & 1)) s_hloc[(a * T + t) * 16 + 4 * wave + r] = hv;
                 }
-                __syncthreads();
+                lds_barrier();
                 if (tid < 8 * T * kMaxItemsInFlight) {
                     const int a = tid / (8 * T), rem = tid - a * 8 * T, t = rem >> 3, mm = rem & 7;
                     const int it = it0 + a * G;
@@ -997,7 +1055,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         }
                     }
                 }
-                __syncthreads();
+                lds_barrier();
             }
         }
         // this workgroup's SwiGLU rows of layer l are stored (every thread's
@@ -1005,27 +1063,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) ll_store(P.fl + (size_t)w * kFLW, base[0] + (uint32_t)l + 1u, 1u);
+        if (w >= U * nch) issue_down_prefetch();     // no items in this workgroup
 
         // -------------------------------------------------------------- DOWN
         {
-            // before waiting for the flags, issue the loads the phase needs
-            // anyway: the next layer's router rows and the down rows of this
-            // thread's first (expert, block) item; they land during the wait
-            float4 rv[kRW];
-            if (l + 1 < L) load_router(l + 1, rv);
-            uint32_t qd0[8][W];
-            float scd0[8];
-            if (tid < U * nkbF && nrows > 0) {
-                const int u = tid / nkbF, kb = tid - u * nkbF;
-                const int e = s_uniq[u];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int rr = min(r, nrows - 1);
-                    const size_t blk = (size_t)l * lstrideD + ((size_t)e * D + d_lo + rr) * nkbF + kb;
-                    load_block<W>(m.down_q, blk, qd0[r]);
-                    scd0[r] = h2f(m.down_s[blk]);
-                }
-            }
             // every workgroup's flag: thread g waits for workgroup g's
             bool ok = true;
             for (int g = tid; g < G; g += kThreads) {
@@ -1034,7 +1075,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                                       [&](int) { return base[0] + (uint32_t)l + 1u; }, pay, 1, P);
             }
             STACK_CHECK_OK(ok);
-            if (l + 1 < L) store_router(rv);
             const uint32_t* hpp = P.hp + (size_t)l * hp_layer;
             constexpr int kTG = T <= 2 ? T : 2;     // tokens whose h halves are held at once
             for (int it = tid; it < U * nkbF; it += kThreads) {
@@ -1078,7 +1118,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                             for (int r = 0; r < 8; ++r) {
 #pragma unroll
                                 for (int k = 0; k < W; ++k) qd[r][k] = qd0[r][k];
-                                scd[r] = scd0[r];
+                                scd[r] = h2f(scd0[r]);
                             }
                         } else {
 #pragma unroll
@@ -1104,7 +1144,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // o[p][r] = sum of blocks in order, one thread per (pair, row)
             float* s_o = s_z_f;                                          // [PT][DPW], reuses the logit area
             for (int o = tid; o < PT * nrows; o += kThreads) {
@@ -1123,7 +1163,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 for (; kb < nkbF; ++kb) oj += pp[kb];
                 s_o[p * DPW + r] = oj;
             }
-            __syncthreads();
+            lds_barrier();
             // y rows (slots in order with their gates), residual, sums of squares
             for (int o = tid; o < T * nrows; o += kThreads) {
                 const int t = o / nrows, r = o - t * nrows;
@@ -1150,7 +1190,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 if (P.h_layers) P.h_layers[((size_t)l * T + t) * D + d] = hn;
                 s_hloc[t * nrows + r] = hn;
             }
-            __syncthreads();
+            lds_barrier();
             if (l + 1 < L && tid < T) {
                 double ss = 0.0;
                 for (int r = 0; r < nrows; ++r) {
