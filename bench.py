@@ -9,9 +9,20 @@ launch (moe_decode_stack).
 Inputs (all 24,576 experts, ~36 GB) are resident in HBM before timing; each
 step consumes a different synthetic token.
 
-Also measured in the same run (reported under "also"): the 8,192-token
-prefill chunk (route + buckets + grouped GEMMs + combine) and the 4-token
-3-bit verify step over 48 layers.
+Also measured in the same run (reported under "also", each with median and
+p10/p90 of the per-step kernel time from HIP events on the launch stream):
+  decode_1layer   single-layer decode at batch 1 (moe_route + moe_ffn_decode),
+                  a 1 GiB buffer rewritten before every step (untimed) so the
+                  layer's weights come from HBM, not the MALL;
+  verify          the 4-token 3-bit verify step over 48 layers;
+  verify6         a 6-token verify step over the 2-bit 48 layers;
+  experts256      a 2-token step over 4 layers of 256 experts;
+  prefill         the 8,192-token chunk through one layer (route + buckets +
+                  grouped GEMMs + combine);
+  prefill_stack   a 32,768-token prompt in 8,192-token chunks through all 48
+                  layers.
+The CPU oracle is timed on bounded samples of the decode, verify and prefill
+workloads (cpu_* below); it is a reported baseline, not a target.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -37,20 +48,34 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # HBM traffic of decode_stack_kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes (see profiles/), valid only for the kernel source it was taken on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack_traffic.json")
-KERNEL_SOURCES = ("quantized_moe_expert_lds_amd/csrc/stack.hip", "quantized_moe_expert_lds_amd/csrc/common.hpp")
+KERNEL_SOURCES = ("quantized_moe_expert_lds_amd/csrc/stack_kernel.hpp", "quantized_moe_expert_lds_amd/csrc/stack.hip",
+                  "quantized_moe_expert_lds_amd/csrc/stack.hpp", "quantized_moe_expert_lds_amd/csrc/common.hpp")
 COPY_BYTES = 1 << 30
+FLUSH_BYTES = 1 << 30
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_stack(q, torch, wl, bits=None):
+def stats_us(seconds):
+    """median, p10, p90 and mean of per-step times, in microseconds."""
+    a = np.asarray(seconds, dtype=np.float64) * 1e6
+    return {"median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "mean_us": float(a.mean()), "n": int(a.size)}
+
+
+def expert_bytes(D, F, bits):
+    """Packed bytes of one expert: codes and fp16 scales of gate, up and down."""
+    return 3 * D * F // 32 * (4 * (2 if bits == 2 else 3) + 2)
+
+
+def build_stack(q, torch, wl, bits=None, n_layers=None):
     """Every layer of a workload as one Stack, generated in HBM."""
     import moe_inputs.gpu as g
     bits = wl.bits if bits is None else bits
-    ex = g.expert_tensors(wl, None, bits)
-    rt = g.routers(wl)
+    ex = g.expert_tensors(wl, n_layers, bits)
+    rt = g.routers(wl, n_layers)
     rw = torch.stack([w for w, _ in rt]).contiguous()
     rb = torch.stack([b for _, b in rt]).contiguous() if wl.zipf_bias else None
     del rt
@@ -59,18 +84,19 @@ def build_stack(q, torch, wl, bits=None):
     return st, (ex, rw, rb)
 
 
-def bench_stack(q, torch, wl, steps, warmup, bits=None, built=None):
+def bench_stack(q, torch, wl, steps, warmup, built, n_tokens=None):
     """Time `steps` decode steps (one moe_decode_stack launch each, a new
-    token batch per step) after `warmup` steps.  Returns wall seconds per step,
-    the average kernel duration from HIP events on the launch stream, and the
-    algorithmic HBM bytes per launch (packed codes + scales of the distinct
-    experts each layer selects, the router matrices, activations).  `built`
-    is a (Stack, tensors) pair from build_stack to reuse; it is not freed."""
+    token batch per step) after `warmup` steps, on the Stack in `built`.
+    Returns wall seconds per step, the per-step kernel durations from HIP
+    events on the launch stream, the algorithmic HBM bytes per launch (packed
+    codes + scales of the distinct experts each layer selects, the router
+    matrices, activations) and the mean distinct experts per layer."""
     import moe_inputs.gpu as g
-    st, keep = build_stack(q, torch, wl, bits) if built is None else built
-    T, L, K, D, E = wl.n_tokens, st.n_layers, wl.top_k, wl.d_model, wl.n_experts
+    st = built[0]
+    T = wl.n_tokens if n_tokens is None else n_tokens
+    L, K, D, E = st.n_layers, wl.top_k, wl.d_model, wl.n_experts
     n_tok = steps + warmup
-    xs = torch.stack([g.activations(wl, stream=s) for s in range(n_tok)])
+    xs = torch.stack([g.activations(wl, T, stream=s) for s in range(n_tok)])
     h = torch.empty((T, D), device="cuda")
     ws = q.stack_workspace(st, T)
     ids = torch.empty((steps, L, T, K), dtype=torch.int32, device="cuda")
@@ -87,21 +113,73 @@ def bench_stack(q, torch, wl, steps, warmup, bits=None, built=None):
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    kern = [a.elapsed_time(b) * 1e-3 for a, b in ev]
     err = int(ws[q.MOE_STACK_ERROR_OFFSET:q.MOE_STACK_ERROR_OFFSET + 4].view(torch.int32).item())
     if err:
-        raise RuntimeError("moe_decode_stack reported a barrier timeout")
+        raise RuntimeError("moe_decode_stack reported a wait timeout")
     ids_np = ids.cpu().numpy()
     uniq = np.array([[len(np.unique(ids_np[i, l])) for l in range(L)] for i in range(steps)])
-    bits_ = st._c.bits
-    per_expert = 3 * D * wl.d_ff // 32 * (4 * (2 if bits_ == 2 else 3) + 2)
-    nbytes = float(uniq.sum(axis=1).mean()) * per_expert + L * E * D * 4 + (E * 4 * L if wl.zipf_bias else 0) \
-        + 2 * T * D * 4
-    del xs, ws
-    if built is None:
-        del st, keep
-    torch.cuda.empty_cache()
+    nbytes = float(uniq.sum(axis=1).mean()) * expert_bytes(D, wl.d_ff, st._c.bits) + L * E * D * 4 \
+        + (E * 4 * L if wl.zipf_bias else 0) + 2 * T * D * 4
+    del xs, ws, h, ids, gw
     return wall, kern, nbytes, float(uniq.mean())
+
+
+def stack_line(name, T, L, E, bits, wall, kern, nbytes, uniq):
+    k = stats_us(kern)
+    rate = nbytes / (k["mean_us"] * 1e-6) / 1e9
+    return {"workload": name, "tokens": T, "layers": L, "experts_per_layer": E, "weight_bits": bits,
+            "tokens_per_s": T / wall, "ms_per_step": wall * 1e3, "kernel_us": k,
+            "us_per_layer_median": k["median_us"] / L, "distinct_experts_per_layer": uniq,
+            "hbm_gbs": rate, "hbm_frac": rate / HBM_PEAK_GBS}
+
+
+def bench_decode_1layer(q, torch, steps=100, warmup=10):
+    """Single-layer decode at batch 1 (bf16 activations): moe_route then
+    moe_ffn_decode, each step after an untimed rewrite of a 1 GiB buffer so
+    no weights of the layer are left in the MALL.  Returns kernel times of
+    the route, the expert FFN and both, and the FFN's achieved HBM rate
+    (packed bytes of the 10 selected experts + activations in and out)."""
+    import moe_inputs as mi
+    import moe_inputs.gpu as g
+    wl = mi.WORKLOADS["decode_1layer"]
+    ex = g.expert_tensors(wl, 1)
+    (w, b), = g.routers(wl, 1)
+    router = q.Router(w, b, wl.top_k)
+    experts = q.Experts(ex["gate_q"][0], ex["up_q"][0], ex["down_q"][0], ex["gate_s"][0], ex["up_s"][0],
+                        ex["down_s"][0], wl.bits)
+    T, K, E, D, F = 1, wl.top_k, wl.n_experts, wl.d_model, wl.d_ff
+    xs = [g.activations(wl, 1, stream=s) for s in range(steps + warmup)]
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, K), device="cuda")
+    y = torch.empty((T, D), device="cuda")
+    ws_r = q.workspace(q.MOE_OP_ROUTE, T, D, F, E, K)
+    ws_d = q.workspace(q.MOE_OP_DECODE, T, D, F, E, K)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = []
+    for i in range(steps + warmup):
+        flush.add_(1.0)
+        a, m, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        q.moe_route(router, xs[i], ids, gw, None, None, ws_r)
+        m.record(stream)
+        q.moe_ffn_decode(experts, xs[i], ids, gw, y, ws_d)
+        b.record(stream)
+        if i >= warmup:
+            ev.append((a, m, b))
+    torch.cuda.synchronize()
+    route_s = [a.elapsed_time(m) * 1e-3 for a, m, b in ev]
+    ffn_s = [m.elapsed_time(b) * 1e-3 for a, m, b in ev]
+    both = [r + f for r, f in zip(route_s, ffn_s)]
+    ffn_bytes = K * expert_bytes(D, F, wl.bits) + T * D * 2 + T * D * 4
+    f_med = float(np.median(ffn_s))
+    res = {"workload": "decode_1layer", "route_us": stats_us(route_s), "ffn_us": stats_us(ffn_s),
+           "layer_us": stats_us(both), "target_us": 2.63,
+           "ffn_hbm_gbs": ffn_bytes / f_med / 1e9, "ffn_hbm_frac": ffn_bytes / f_med / 1e9 / HBM_PEAK_GBS,
+           "mall_flush_bytes": FLUSH_BYTES}
+    del ex, flush, xs, ws_r, ws_d, router, experts
+    return res
 
 
 def bench_prefill_stack(q, torch, st, steps=2, warmup=1):
@@ -128,52 +206,17 @@ def bench_prefill_stack(q, torch, st, steps=2, warmup=1):
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    gpu_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    gpu_s = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in ev]))
     L, K, D, F = st.n_layers, st.top_k, st.d_model, wl.d_ff
     flops = 2.0 * T * K * 3 * D * F * L
     res = {"workload": "prefill_32k_48layer", "tokens": T, "chunk": chunk, "layers": L,
            "tokens_per_s": T / wall, "ms_per_prompt": wall * 1e3, "gpu_ms_per_prompt": gpu_s * 1e3,
            "ffn_tflops_incl_routing": flops / gpu_s / 1e12}
     del x, h, ws
-    torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(n_layers_sample=12):
-    """The oracle (numpy) on the host cores: the first n layers of the 48-layer
-    bs1 chain; expert generation (input preparation) is done before timing."""
-    import moe_inputs as mi
-    from moe_inputs import host_cache
-    import oracle.moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
-    wl = mi.WORKLOADS["decode_48layer"]
-    x = mi.activations_host(wl)
-    # input preparation: route through the sample once to learn which experts
-    # are touched and generate them (untimed)
-    h = x.copy()
-    routers = [mi.router_host(wl, l) for l in range(n_layers_sample)]
-    for l in range(n_layers_sample):
-        u = h if l == 0 else O.rmsnorm(h)
-        ids, _, _ = O.route(u, routers[l][0], routers[l][1], wl.top_k)
-        host_cache.prefetch(wl.name, l, np.unique(ids), wl.bits)
-        _, _, y = O.moe_layer(u, routers[l][0], routers[l][1], wl.top_k, host_cache.experts_of(wl, l), wl.bits)
-        h = (h + y).astype(np.float32)
-    t0 = time.perf_counter()
-    O.moe_chain(x, n_layers_sample, lambda l: routers[l], lambda l: host_cache.experts_of(wl, l), wl.top_k,
-                wl.bits)
-    dt = time.perf_counter() - t0
-    per_token = dt * wl.n_layers / n_layers_sample
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": int(blas_threads),
-            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"first {n_layers_sample} of 48 layers of one bs1 decode step, scaled to 48 layers "
-                      f"({dt:.1f} s measured; expert generation excluded)"}
-
-
-def bench_prefill(q, torch, steps=5, warmup=2):
+def bench_prefill(q, torch, steps=20, warmup=3):
     import moe_inputs as mi
     import moe_inputs.gpu as g
     wl = mi.WORKLOADS["prefill_8192"]
@@ -192,13 +235,9 @@ def bench_prefill(q, torch, steps=5, warmup=2):
     ws_r = q.workspace(q.MOE_OP_ROUTE, T, D, F, E, K)
     ws_p = q.workspace(q.MOE_OP_PREFILL, T, D, F, E, K)
     stream = torch.cuda.current_stream()
-
-    def step():
+    for _ in range(warmup):
         q.moe_route(router, x, ids, gw, off, prs, ws_r)
         q.moe_ffn_prefill(experts, x, gw, off, prs, y, ws_p)
-
-    for _ in range(warmup):
-        step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -211,25 +250,88 @@ def bench_prefill(q, torch, steps=5, warmup=2):
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    route_s = float(np.mean([a.elapsed_time(m) for a, m, b in ev])) * 1e-3
-    ffn_s = float(np.mean([m.elapsed_time(b) for a, m, b in ev])) * 1e-3
+    route_s = [a.elapsed_time(m) * 1e-3 for a, m, b in ev]
+    ffn_s = [m.elapsed_time(b) * 1e-3 for a, m, b in ev]
     flops = 2.0 * T * K * 3 * D * F
+    f_med = float(np.median(ffn_s))
     res = {"workload": "prefill_8192", "tokens_per_s": T / wall, "ms_per_step": wall * 1e3,
-           "route_ms": route_s * 1e3, "ffn_ms": ffn_s * 1e3,
-           "ffn_tflops": flops / ffn_s / 1e12, "ffn_mfma_frac": flops / ffn_s / 1e12 / MFMA_F16_PEAK_TFLOPS}
-    del ex, ws_p
-    torch.cuda.empty_cache()
+           "route_us": stats_us(route_s), "ffn_us": stats_us(ffn_s),
+           "ffn_tflops": flops / f_med / 1e12, "ffn_mfma_frac": flops / f_med / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    del ex, ws_p, ws_r, x, y, ids, gw, off, prs, router, experts
     return res
 
 
-def bench_verify(q, torch, steps=10, warmup=3):
+# ------------------------------------------------------------ CPU baselines
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def _cpu_chain(wl, n_tokens, n_layers):
+    """Seconds of the oracle's residual chain over the first n_layers of a
+    workload for n_tokens tokens.  The touched experts are generated first by
+    routing through the sample once (input preparation, untimed)."""
+    import moe_inputs as mi
+    from moe_inputs import host_cache
+    import oracle.moe_oracle as O
+    x = mi.activations_host(wl, n_tokens)
+    routers = [mi.router_host(wl, l) for l in range(n_layers)]
+    routers = [(w, b if wl.zipf_bias else None) for w, b in routers]
+    O.moe_chain(x, n_layers, lambda l: routers[l], lambda l: host_cache.experts_of(wl, l), wl.top_k, wl.bits,
+                prepare_of=lambda l: (lambda ids: host_cache.prefetch(wl.name, l, ids, wl.bits)))
+    t0 = time.perf_counter()
+    O.moe_chain(x, n_layers, lambda l: routers[l], lambda l: host_cache.experts_of(wl, l), wl.top_k, wl.bits)
+    return time.perf_counter() - t0
+
+
+def cpu_decode():
+    """All 48 layers of one bs1 decode step through the oracle."""
+    import moe_inputs as mi
+    wl = mi.WORKLOADS["decode_48layer"]
+    dt = _cpu_chain(wl, 1, wl.n_layers)
+    return {"value": 1.0 / dt, "unit": "tokens/s", "cores": _blas_threads(),
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"one bs1 decode step, all 48 layers ({dt:.1f} s; expert generation excluded)"}
+
+
+def cpu_verify(n_layers=12):
+    """The 4-token 3-bit verify step through the first n_layers, scaled."""
     import moe_inputs as mi
     wl = mi.WORKLOADS["verify4_3bit"]
-    wall, kern, nbytes, uniq = bench_stack(q, torch, wl, steps, warmup)
-    return {"workload": "verify4_3bit", "tokens_per_s": wl.n_tokens / wall, "ms_per_step": wall * 1e3,
-            "kernel_ms": kern * 1e3, "distinct_experts_per_layer": uniq,
-            "hbm_gbs": nbytes / kern / 1e9, "hbm_frac": nbytes / kern / 1e9 / HBM_PEAK_GBS}
+    dt = _cpu_chain(wl, wl.n_tokens, n_layers)
+    per_step = dt * wl.n_layers / n_layers
+    return {"value": wl.n_tokens / per_step, "unit": "tokens/s", "cores": _blas_threads(),
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"4 tokens through the first {n_layers} of 48 layers ({dt:.1f} s), scaled to 48 layers; "
+                      "expert generation excluded"}
 
+
+def cpu_prefill(n_tokens=128):
+    """The first n_tokens of the 8,192-token chunk through the layer (route,
+    experts, combine) by the oracle."""
+    import moe_inputs as mi
+    from moe_inputs import host_cache
+    import oracle.moe_oracle as O
+    wl = mi.WORKLOADS["prefill_8192"]
+    x = mi.activations_host(wl)[:n_tokens]
+    w, b = mi.router_host(wl, 0)
+    b = b if wl.zipf_bias else None
+    ids, _, _ = O.route(x, w, b, wl.top_k)
+    host_cache.prefetch(wl.name, 0, np.unique(ids), wl.bits)
+    t0 = time.perf_counter()
+    O.moe_layer(x, w, b, wl.top_k, host_cache.experts_of(wl, 0), wl.bits)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": _blas_threads(),
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"first {n_tokens} of the 8,192 tokens through the layer ({dt:.1f} s; "
+                      f"{len(np.unique(ids))} experts touched, their generation excluded)"}
+
+
+# ------------------------------------------------------------ counters
 
 def kernel_source_hash():
     h = hashlib.sha256()
@@ -258,39 +360,32 @@ def profile_pass(q, torch):
     written once) that calibrates the counters."""
     import moe_inputs as mi
     wl = mi.WORKLOADS["decode_48layer"]
-    bench_stack(q, torch, wl, 3, 1)
+    built = build_stack(q, torch, wl)
+    bench_stack(q, torch, wl, 3, 1, built)
+    del built
     src = torch.ones(COPY_BYTES // 4, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(2):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
+    del src, dst
     print(json.dumps({"profile_pass": "decode_48layer x3 + copy", "copy_bytes": COPY_BYTES,
                       "kernel_source_sha256": kernel_source_hash()}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-also", action="store_true", help="skip the prefill and verify workloads")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="only 3 decode steps and a calibration copy, for rocprofv3 counter passes")
-    ap.add_argument("--prefill-pass", action="store_true",
-                    help="only the 8,192-token prefill chunk (3 timed calls), for rocprofv3 passes")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the MoE FFN path is built and measured on a single MI355X "
-              "(all experts resident in its HBM); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def teardown(torch):
+    """Orderly end, once every GPU tensor of the run is released: finish the
+    device work, return the cached blocks and stop the host worker pool
+    before the interpreter (and a profiler attached to it) shuts down."""
+    from moe_inputs import host_cache
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    host_cache.shutdown()
+    host_cache.clear()
 
-    import torch
+
+def run(args, q, torch):
     import moe_inputs as mi
-    import moe_inputs.gpu as g
-    import quantized_moe_expert_lds_amd as q
-
-    torch.cuda.set_device(0)
     if args.profile_pass:
         profile_pass(q, torch)
         return
@@ -300,26 +395,49 @@ def main():
     wl = mi.WORKLOADS["decode_48layer"]
     log("48-layer decode, batch 1: generating 48 x 512 experts in HBM and timing")
     built = build_stack(q, torch, wl)
-    dt, kern, nbytes, uniq = bench_stack(q, torch, wl, args.steps, args.warmup, built=built)
-    achieved = nbytes / kern / 1e9
-    log(f"decode step {dt * 1e6:.1f} us wall, kernel {kern * 1e6:.1f} us, {achieved:.0f} GB/s")
+    dt, kern, nbytes, uniq = bench_stack(q, torch, wl, args.steps, args.warmup, built)
+    k = stats_us(kern)
+    achieved = nbytes / (k["mean_us"] * 1e-6) / 1e9
+    log(f"decode step {dt * 1e6:.1f} us wall, kernel median {k['median_us']:.1f} us, {achieved:.0f} GB/s")
 
     also = {}
     if not args.no_also:
+        log("verify, 6 tokens, 2-bit 48 layers")
+        r = bench_stack(q, torch, wl, 30, 5, built, n_tokens=6)
+        also["verify6"] = stack_line("verify6_2bit", 6, wl.n_layers, wl.n_experts, 2, *r)
         log("prefill of a 32,768-token prompt through the 48 layers")
         also["prefill_stack"] = bench_prefill_stack(q, torch, built[0])
     del built
     torch.cuda.empty_cache()
     if not args.no_also:
+        log("single-layer decode with a MALL flush")
+        also["decode_1layer"] = bench_decode_1layer(q, torch)
+        torch.cuda.empty_cache()
         log("prefill 8192")
         also["prefill"] = bench_prefill(q, torch)
+        torch.cuda.empty_cache()
         log("verify 4 tokens 3-bit")
-        also["verify"] = bench_verify(q, torch)
+        wv = mi.WORKLOADS["verify4_3bit"]
+        bv = build_stack(q, torch, wv)
+        r = bench_stack(q, torch, wv, 100, 10, bv)
+        also["verify"] = stack_line("verify4_3bit", 4, wv.n_layers, wv.n_experts, 3, *r)
+        del bv
+        torch.cuda.empty_cache()
+        log("256 experts, 2 tokens, 4 layers")
+        wc = mi.WORKLOADS["coder_256"]
+        bc = build_stack(q, torch, wc)
+        r = bench_stack(q, torch, wc, 100, 10, bc)
+        also["experts256"] = stack_line("coder_256", wc.n_tokens, wc.n_layers, wc.n_experts, 2, *r)
+        del bc
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
-        log("CPU oracle baseline")
-        cpu = cpu_baseline()
+        log("CPU oracle baselines")
+        cpu = cpu_decode()
+        if not args.no_also:
+            also["verify"]["cpu_baseline"] = cpu_verify()
+            also["prefill"]["cpu_baseline"] = cpu_prefill()
 
     out = {
         "metric": METRIC,
@@ -337,15 +455,41 @@ def main():
                 "Zipf-biased router)",
         "config": {"workload": "decode_48layer", "layers": 48, "experts_per_layer": 512, "d_model": 2048,
                    "d_ff": 768, "top_k": 10, "batch": 1, "weight_bits": 2, "parallelism": "single GPU"},
+        "step_kernel_us": k,
         "roofline": {"bound": "hbm", "kernel": "decode_stack_kernel (all 48 layers, one launch)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "bytes_per_launch": nbytes, "kernel_us": kern * 1e6,
+                     "bytes_per_launch": nbytes, "kernel_us": k["mean_us"],
                      "distinct_experts_per_layer": uniq},
         "cpu_baseline": cpu,
         "also": also,
     }
     print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="only 3 decode steps and a calibration copy, for rocprofv3 counter passes")
+    ap.add_argument("--prefill-pass", action="store_true",
+                    help="only the 8,192-token prefill chunk (3 timed calls), for rocprofv3 passes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MoE FFN path is built and measured on a single MI355X "
+              "(all experts resident in its HBM); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_moe_expert_lds_amd as q
+
+    torch.cuda.set_device(0)
+    run(args, q, torch)
+    teardown(torch)
 
 
 if __name__ == "__main__":
