@@ -6,9 +6,10 @@ seeded token and run their own chain; the GPU's per-layer residuals
 (``moe_decode_stack``'s h_layers output) are compared with the oracle's
 layer by layer, token by token.
 
-Where the two chains may legitimately part ways.  The GPU rounds the
-activations and the SwiGLU intermediate to fp16, so its residual drifts from
-the oracle's by ~1e-4 relative over the layers.  Routing then sees logits
+Where the two chains may legitimately part ways.  The GPU carries the
+activations and the SwiGLU intermediate as fp16 (the layer-by-layer calls) or
+as two fp16 halves (the whole-step kernel), so its residual drifts from the
+oracle's over the layers (~1e-4 and ~1e-7 relative).  Routing then sees logits
 z(u_gpu) instead of z(u_oracle); expert e's logit moves by dz_e = (u_gpu -
 u_oracle) . w_e (both routers accumulate in fp64, so summation order adds
 only ~1e-15).  Two experts a, b can swap ranks only if the oracle's margin
