@@ -19,6 +19,8 @@ p10/p90 of the per-step kernel time from HIP events on the launch stream):
   experts256      a 2-token step over 4 layers of 256 experts;
   prefill         the 8,192-token chunk through one layer (route + buckets +
                   grouped GEMMs + combine);
+  prefill_int8    the same chunk with the int8-activation expert FFN
+                  (moe_ffn_prefill_q8);
   prefill_stack   a 32,768-token prompt in 8,192-token chunks through all 48
                   layers.
 The CPU oracle is timed on bounded samples of the decode, verify and prefill
@@ -45,6 +47,9 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN tokens/s: 48-layer decode (bs1, bs4) + 8192-tok prefill; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_I8_PEAK_TOPS = 5000.0
+# non-packed fp32 vector instructions: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
 # HBM traffic of decode_stack_kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes (see profiles/), valid only for the kernel source it was taken on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack_traffic.json")
@@ -216,7 +221,10 @@ def bench_prefill_stack(q, torch, st, steps=2, warmup=1):
     return res
 
 
-def bench_prefill(q, torch, steps=20, warmup=3):
+def bench_prefill(q, torch, steps=20, warmup=3, int8=False):
+    """The 8,192-token chunk through one layer: moe_route (with buckets),
+    then the expert FFN, moe_ffn_prefill (fp16 matrix cores) or, with int8,
+    moe_ffn_prefill_q8 (int8 activations on the int8 matrix cores)."""
     import moe_inputs as mi
     import moe_inputs.gpu as g
     wl = mi.WORKLOADS["prefill_8192"]
@@ -233,11 +241,12 @@ def bench_prefill(q, torch, steps=20, warmup=3):
     prs = torch.empty(T * K, dtype=torch.int32, device="cuda")
     y = torch.empty((T, D), device="cuda")
     ws_r = q.workspace(q.MOE_OP_ROUTE, T, D, F, E, K)
-    ws_p = q.workspace(q.MOE_OP_PREFILL, T, D, F, E, K)
+    ws_p = q.workspace(q.MOE_OP_PREFILL_Q8 if int8 else q.MOE_OP_PREFILL, T, D, F, E, K)
+    ffn = q.moe_ffn_prefill_q8 if int8 else q.moe_ffn_prefill
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         q.moe_route(router, x, ids, gw, off, prs, ws_r)
-        q.moe_ffn_prefill(experts, x, gw, off, prs, y, ws_p)
+        ffn(experts, x, gw, off, prs, y, ws_p)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -246,7 +255,7 @@ def bench_prefill(q, torch, steps=20, warmup=3):
         a.record(stream)
         q.moe_route(router, x, ids, gw, off, prs, ws_r)
         m.record(stream)
-        q.moe_ffn_prefill(experts, x, gw, off, prs, y, ws_p)
+        ffn(experts, x, gw, off, prs, y, ws_p)
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
@@ -254,9 +263,16 @@ def bench_prefill(q, torch, steps=20, warmup=3):
     ffn_s = [m.elapsed_time(b) * 1e-3 for a, m, b in ev]
     flops = 2.0 * T * K * 3 * D * F
     f_med = float(np.median(ffn_s))
-    res = {"workload": "prefill_8192", "tokens_per_s": T / wall, "ms_per_step": wall * 1e3,
-           "route_us": stats_us(route_s), "ffn_us": stats_us(ffn_s),
-           "ffn_tflops": flops / f_med / 1e12, "ffn_mfma_frac": flops / f_med / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    res = {"workload": "prefill_8192_int8" if int8 else "prefill_8192", "tokens_per_s": T / wall,
+           "ms_per_step": wall * 1e3, "route_us": stats_us(route_s), "ffn_us": stats_us(ffn_s)}
+    if int8:
+        # int8 multiply-adds at the int8 MFMA peak, and the vector-unit floor
+        # of the block scaling: 3 instructions per output and 32-block
+        res.update({"ffn_tops": flops / f_med / 1e12, "ffn_i8_frac": flops / f_med / 1e12 / MFMA_I8_PEAK_TOPS,
+                    "valu_floor_us": 3.0 * T * K * (2 * F * D / 32 + D * F / 32) / VALU_LANE_OPS_PER_S * 1e6})
+    else:
+        res.update({"ffn_tflops": flops / f_med / 1e12,
+                    "ffn_mfma_frac": flops / f_med / 1e12 / MFMA_F16_PEAK_TFLOPS})
     del ex, ws_p, ws_r, x, y, ids, gw, off, prs, router, experts
     return res
 
@@ -331,6 +347,28 @@ def cpu_prefill(n_tokens=128):
                       f"{len(np.unique(ids))} experts touched, their generation excluded)"}
 
 
+def cpu_prefill_q8(n_tokens=128):
+    """The int8-activation oracle variant on the first n_tokens of the
+    8,192-token chunk (routing by the oracle, untimed)."""
+    import moe_inputs as mi
+    from moe_inputs import host_cache
+    import oracle.moe_oracle as O
+    import oracle.moe_oracle_q8 as Q
+    wl = mi.WORKLOADS["prefill_8192"]
+    x = mi.activations_host(wl)[:n_tokens]
+    w, b = mi.router_host(wl, 0)
+    b = b if wl.zipf_bias else None
+    ids, gates, _ = O.route(x, w, b, wl.top_k)
+    host_cache.prefetch(wl.name, 0, np.unique(ids), wl.bits)
+    t0 = time.perf_counter()
+    Q.moe_layer_q8(x, ids, gates, host_cache.experts_of(wl, 0))
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": _blas_threads(),
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"int8 variant, first {n_tokens} of the 8,192 tokens, expert FFN only ({dt:.1f} s; "
+                      f"{len(np.unique(ids))} experts touched, their generation excluded)"}
+
+
 # ------------------------------------------------------------ counters
 
 def kernel_source_hash():
@@ -391,6 +429,7 @@ def run(args, q, torch):
         return
     if args.prefill_pass:
         print(json.dumps(bench_prefill(q, torch, steps=3, warmup=1)), flush=True)
+        print(json.dumps(bench_prefill(q, torch, steps=3, warmup=1, int8=True)), flush=True)
         return
     wl = mi.WORKLOADS["decode_48layer"]
     log("48-layer decode, batch 1: generating 48 x 512 experts in HBM and timing")
@@ -416,6 +455,9 @@ def run(args, q, torch):
         log("prefill 8192")
         also["prefill"] = bench_prefill(q, torch)
         torch.cuda.empty_cache()
+        log("prefill 8192, int8 activations")
+        also["prefill_int8"] = bench_prefill(q, torch, int8=True)
+        torch.cuda.empty_cache()
         log("verify 4 tokens 3-bit")
         wv = mi.WORKLOADS["verify4_3bit"]
         bv = build_stack(q, torch, wv)
@@ -438,6 +480,7 @@ def run(args, q, torch):
         if not args.no_also:
             also["verify"]["cpu_baseline"] = cpu_verify()
             also["prefill"]["cpu_baseline"] = cpu_prefill()
+            also["prefill_int8"]["cpu_baseline"] = cpu_prefill_q8()
 
     out = {
         "metric": METRIC,

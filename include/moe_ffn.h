@@ -79,6 +79,7 @@ extern "C" {
 #define MOE_OP_ROUTE   0
 #define MOE_OP_DECODE  1
 #define MOE_OP_PREFILL 2
+#define MOE_OP_PREFILL_Q8 3
 
 /* byte offset in a moe_decode_stack workspace of the int that becomes
  * nonzero if a grid barrier timed out (see moe_decode_stack) */
@@ -209,6 +210,40 @@ int moe_ffn_decode_noalloc(const moe_experts_t* experts, const void* x, int x_dt
 int moe_ffn_prefill(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens,
                     const float* topk_w, int top_k, const int32_t* bucket_offsets,
                     const int32_t* bucket_pairs, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Q8 blocks of activations, the int8 format of moe_ffn_prefill_q8 (a
+ * reading of the quantised prefill matmuls of bnskd, section 工程细节, whose
+ * activation format the pages leave open).  Each row is cut into blocks of
+ * 32 consecutive values; per block, in fp32:
+ *   amax = max |v|;  if amax < 2^-112:  q = 0, d = 0
+ *   else:  q[i] = round_half_even(v[i] * (127 / amax)) in [-127, 127],
+ *          d = amax / 127      (both divisions correctly rounded)
+ * so v[i] ~ q[i] * d within d / 2.
+ *
+ *   x  device [n_rows][n_cols], fp32 or bf16 (x_dtype)
+ *   q  device int8 [n_rows][n_cols] (output)
+ *   d  device fp32 [n_rows][n_cols / 32] (output)
+ * Supported: n_cols a multiple of 32.  No workspace. */
+int moe_quantize_q8(const void* x, int x_dtype, int n_rows, int n_cols, int8_t* q, float* d, void* stream);
+
+/* Expert FFN and combine for a prefill chunk with int8 activations on the
+ * int8 matrix cores, the pages' way of running prefill matmuls on quantised
+ * operands (bnskd, section 工程细节).  Same arguments and routing inputs as
+ * moe_ffn_prefill, workspace moe_workspace_size(MOE_OP_PREFILL_Q8, ...).
+ *   x -> Q8 blocks (moe_quantize_q8);  for each pair (t, j) of expert e:
+ *     g, u = sum over blocks b of d_x[t][b] * s[f][b] * sum_k q_x[t][k] * level[f][k]
+ *     h = silu(g) * u  -> Q8 blocks (d_h, q_h)
+ *     o = sum over blocks b of d_h[b] * s_down[n][b] * sum_k q_h[k] * level_down[n][k]
+ *   y[t] = sum_j topk_w[t][j] * o(t, j), in ascending j
+ * The block sums are exact int32 products of int8 codes and 2-bit levels;
+ * scaling and the sums over blocks are fp32.  The result differs from
+ * moe_ffn_prefill's by the int8 rounding of x and h (about 1e-2 of a row's
+ * largest value).
+ * Supported: as moe_ffn_prefill (bits == 2, d_model % 256 == 0,
+ * d_ff % 128 == 0). */
+int moe_ffn_prefill_q8(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens,
+                       const float* topk_w, int top_k, const int32_t* bucket_offsets,
+                       const int32_t* bucket_pairs, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Residual update and RMSNorm between chained layers:
  *   h[t] += y[t];  u[t] = h[t] / sqrt(mean(h[t]^2) + eps)

@@ -22,16 +22,18 @@ __all__ = [
     "MOE_STACK_ERROR_OFFSET", "MoeError", "Router", "Experts", "Stack", "lib_path", "library",
     "moe_workspace_size", "workspace", "moe_route", "moe_ffn_decode", "moe_ffn_prefill", "moe_decode_stack",
     "moe_residual_rmsnorm", "moe_status_string", "EXPORTED_SYMBOLS", "moe_ffn_decode_noalloc",
+    "MOE_OP_PREFILL_Q8", "moe_ffn_prefill_q8", "moe_quantize_q8",
 ]
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_DEVICE, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
-MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
+MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_PREFILL_Q8 = 0, 1, 2, 3
 MOE_STACK_ERROR_OFFSET = 2304
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_ffn_decode", "moe_ffn_decode_noalloc",
                     "moe_ffn_prefill", "moe_stack_workspace_size", "moe_decode_stack", "moe_prefill_stack_workspace_size",
-                    "moe_prefill_stack", "moe_residual_rmsnorm", "moe_status_string")
+                    "moe_prefill_stack", "moe_residual_rmsnorm", "moe_status_string", "moe_ffn_prefill_q8",
+                    "moe_quantize_q8")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "lib", "libmoe_ffn.so")
@@ -78,6 +80,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_ffn_decode_noalloc.restype = I
     lib.moe_ffn_prefill.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, I, P, P, P, P, Z, P]
     lib.moe_ffn_prefill.restype = I
+    lib.moe_ffn_prefill_q8.argtypes = [ctypes.POINTER(_ExpertsT), P, I, I, P, I, P, P, P, P, Z, P]
+    lib.moe_ffn_prefill_q8.restype = I
+    lib.moe_quantize_q8.argtypes = [P, I, I, I, P, P, P]
+    lib.moe_quantize_q8.restype = I
     lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_StackT), I]
     lib.moe_stack_workspace_size.restype = Z
     lib.moe_decode_stack.argtypes = [ctypes.POINTER(_StackT), P, I, I, D, P, P, P, P, P, Z, P]
@@ -267,6 +273,23 @@ def moe_ffn_prefill(experts: Experts, x: torch.Tensor, topk_w: torch.Tensor, buc
                                  topk_w.shape[1], _ptr(bucket_offsets), _ptr(bucket_pairs), _ptr(y), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(stream))
     _check("moe_ffn_prefill", st)
+
+
+def moe_ffn_prefill_q8(experts: Experts, x: torch.Tensor, topk_w: torch.Tensor, bucket_offsets: torch.Tensor,
+                       bucket_pairs: torch.Tensor, y: torch.Tensor, ws: Optional[torch.Tensor], stream=None) -> None:
+    """moe_ffn_prefill with int8 (Q8 block) activations on the int8 matrix
+    cores; workspace of op MOE_OP_PREFILL_Q8."""
+    st = library.moe_ffn_prefill_q8(ctypes.byref(experts._c), _ptr(x), _dtype(x), x.shape[0], _ptr(topk_w),
+                                    topk_w.shape[1], _ptr(bucket_offsets), _ptr(bucket_pairs), _ptr(y), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream))
+    _check("moe_ffn_prefill_q8", st)
+
+
+def moe_quantize_q8(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, stream=None) -> None:
+    """Q8 blocks of the rows of x: int8 codes q (x's shape) and fp32 scales d
+    [rows][cols / 32]."""
+    st = library.moe_quantize_q8(_ptr(x), _dtype(x), x.shape[0], x.shape[1], _ptr(q), _ptr(d), _stream(stream))
+    _check("moe_quantize_q8", st)
 
 
 def moe_stack_workspace_size(stack: Stack, n_tokens: int) -> int:

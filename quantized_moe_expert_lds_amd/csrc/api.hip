@@ -96,7 +96,9 @@ size_t moe_workspace_size(int op, int n_tokens, int d_model, int d_ff, int n_exp
         case MOE_OP_PREFILL:
             if (d_ff <= 0) return 0;
             return prefill_ws_layout(n_tokens, d_model, d_ff, n_experts, top_k).total;
-
+        case MOE_OP_PREFILL_Q8:
+            if (d_ff <= 0) return 0;
+            return prefill_q8_ws_layout(n_tokens, d_model, d_ff, n_experts, top_k).total;
         default:
             return 0;
     }
@@ -185,6 +187,37 @@ int moe_ffn_prefill(const moe_experts_t* experts, const void* x, int x_dtype, in
     if ((st = check_device())) return st;
     return hip_status(launch_prefill(*experts, x, xf, n_tokens, topk_w, top_k, bucket_offsets, bucket_pairs, y,
                                      (char*)ws, L, (hipStream_t)stream));
+}
+
+int moe_ffn_prefill_q8(const moe_experts_t* experts, const void* x, int x_dtype, int n_tokens, const float* topk_w,
+                       int top_k, const int32_t* bucket_offsets, const int32_t* bucket_pairs, float* y, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int st = check_experts(experts);
+    if (st) return st;
+    if (!x || !topk_w || !bucket_offsets || !bucket_pairs || !y || n_tokens <= 0 || top_k <= 0) return MOE_ERR_ARG;
+    const int xf = dtype_flag(x_dtype);
+    if (xf < 0) return MOE_ERR_ARG;
+    if (experts->bits != 2 || experts->d_model % kDownBN || experts->d_ff % kGateUpBN || top_k > kMaxTopK ||
+        top_k > experts->n_experts)
+        return MOE_ERR_UNSUPPORTED;
+    if ((long long)n_tokens * top_k > (1LL << 28)) return MOE_ERR_UNSUPPORTED;
+    const PrefillQ8Ws L = prefill_q8_ws_layout(n_tokens, experts->d_model, experts->d_ff, experts->n_experts, top_k);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    if ((st = check_device())) return st;
+    return hip_status(launch_prefill_q8(*experts, x, xf, n_tokens, topk_w, top_k, bucket_offsets, bucket_pairs, y,
+                                        (char*)ws, L, (hipStream_t)stream));
+}
+
+int moe_quantize_q8(const void* x, int x_dtype, int n_rows, int n_cols, int8_t* q, float* d, void* stream) {
+    if (!x || !q || !d || n_rows <= 0 || n_cols <= 0) return MOE_ERR_ARG;
+    const int xf = dtype_flag(x_dtype);
+    if (xf < 0) return MOE_ERR_ARG;
+    if (n_cols % 32) return MOE_ERR_UNSUPPORTED;
+    const size_t nblocks = (size_t)n_rows * (size_t)(n_cols / 32);
+    if (nblocks > (size_t(1) << 36)) return MOE_ERR_UNSUPPORTED;
+    int st = check_device();
+    if (st) return st;
+    return hip_status(launch_quantize_q8(x, xf, nblocks, q, d, (hipStream_t)stream));
 }
 
 size_t moe_stack_workspace_size(const moe_stack_t* m, int n_tokens) {

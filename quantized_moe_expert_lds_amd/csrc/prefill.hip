@@ -387,6 +387,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 namespace qmoe {
 
+hipError_t launch_prefill_tiles(const int32_t* offsets, int E, int P, int max_tiles, int4* tiles, int* ntiles,
+                                hipStream_t s) {
+    tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, P, max_tiles, tiles, ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_combine(const float* obuf, int T, int K, int D, float* y, hipStream_t s) {
+    const size_t n4 = (size_t)T * D / 4;
+    combine_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(obuf, T, K, D, y);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const moe_experts_t& ex, const void* x, int x_bf16, int T, const float* gates, int K,
                           const int32_t* offsets, const int32_t* pairs, float* y, char* ws, const PrefillWs& L,
                           hipStream_t s) {

@@ -109,3 +109,41 @@ def test_prefill_stack_validation_before_any_device_call(lib):
     args = list(ok_args(st))
     args[8] = args[8] - 1                                     # workspace one byte short
     assert call(*args) == -3
+
+
+def test_prefill_q8_sizes_and_validation(lib):
+    """The int8-activation prefill's workspace and host-side argument checks
+    (no device call is reached)."""
+    import quantized_moe_expert_lds_amd as q
+    lib.moe_workspace_size.restype = ctypes.c_size_t
+    T, D, F, E, K = 8192, 2048, 768, 512, 10
+    P = T * K
+    n = lib.moe_workspace_size(3, T, D, F, E, K)
+    # int8 x and h, their block scales, fp32 gated output per pair
+    assert n >= T * D + T * D // 32 * 4 + P * F + P * F // 32 * 4 + P * D * 4
+    assert lib.moe_workspace_size(3, T, D, 0, E, K) == 0
+    V = ctypes.c_void_p
+    fake = V(256)
+    call = lib.moe_ffn_prefill_q8
+    call.argtypes = [ctypes.POINTER(q._ExpertsT), V, ctypes.c_int, ctypes.c_int, V, ctypes.c_int, V, V, V, V,
+                     ctypes.c_size_t, V]
+    call.restype = ctypes.c_int
+    def ex(bits=2, d=D, f=F):
+        return q._ExpertsT(E, d, f, bits, fake, fake, fake, fake, fake, fake)
+    args = lambda e, n_tok=64, ws=n, dtype=1: (ctypes.byref(e), fake, dtype, n_tok, fake, K, fake, fake, fake, fake,
+                                               ws, None)
+    assert call(None, fake, 1, 64, fake, K, fake, fake, fake, fake, n, None) == -1
+    assert call(*args(ex(), n_tok=0)) == -1
+    assert call(*args(ex(), dtype=5)) == -1
+    assert call(*args(ex(bits=3))) == -2                      # the int8 path covers the 2-bit format
+    assert call(*args(ex(d=2080))) == -2
+    assert call(*args(ex(f=800))) == -2
+    small = lib.moe_workspace_size(3, 64, D, F, E, K)
+    assert call(*args(ex(), ws=small - 1)) == -3
+    qz = lib.moe_quantize_q8
+    qz.argtypes = [V, ctypes.c_int, ctypes.c_int, ctypes.c_int, V, V, V]
+    qz.restype = ctypes.c_int
+    assert qz(None, 0, 4, 64, fake, fake, None) == -1
+    assert qz(fake, 0, 0, 64, fake, fake, None) == -1
+    assert qz(fake, 3, 4, 64, fake, fake, None) == -1
+    assert qz(fake, 0, 4, 48, fake, fake, None) == -2         # rows cut into blocks of 32
