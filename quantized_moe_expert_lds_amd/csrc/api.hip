@@ -4,7 +4,7 @@
 #include <atomic>
 #include <cstring>
 
-#include "common.hpp"
+#include "prefill_q8.hpp"
 
 namespace qmoe {
 bool decode_supported(int T, int K, int F);

@@ -37,11 +37,6 @@ struct DecodeWs {
 struct PrefillWs {
     size_t x16, hbuf, obuf, tiles, ntiles, total;
 };
-// int8-activation prefill: Q8 codes and scales of x and of h, per-pair
-// rows, the tile list
-struct PrefillQ8Ws {
-    size_t xq, xd, hq, hd, obuf, tiles, ntiles, total;
-};
 struct StackWs {
     size_t hdr, rows, logits, flags, hp, total;
 };
@@ -114,28 +109,6 @@ inline PrefillWs prefill_ws_layout(int T, int D, int F, int E, int K) {
     return w;
 }
 
-inline PrefillQ8Ws prefill_q8_ws_layout(int T, int D, int F, int E, int K) {
-    PrefillQ8Ws w{};
-    size_t off = 0;
-    const size_t P = (size_t)T * K;
-    w.xq = off;
-    off += align256((size_t)T * D);
-    w.xd = off;
-    off += align256(sizeof(float) * (size_t)T * (D / 32));
-    w.hq = off;
-    off += align256(P * F);
-    w.hd = off;
-    off += align256(sizeof(float) * P * (F / 32));
-    w.obuf = off;
-    off += align256(sizeof(float) * P * D);
-    w.tiles = off;
-    off += align256(sizeof(int4) * (size_t)prefill_max_tiles(T, E, K));
-    w.ntiles = off;
-    off += align256(sizeof(int) * 4);
-    w.total = off;
-    return w;
-}
-
 inline PrefillStackWs prefill_stack_ws_layout(int Tc, int D, int F, int E, int K) {
     PrefillStackWs w{};
     const size_t P = (size_t)Tc * K;
@@ -175,14 +148,6 @@ hipError_t launch_decode(const moe_experts_t& ex, const void* x, int x_bf16, int
 hipError_t launch_prefill(const moe_experts_t& ex, const void* x, int x_bf16, int T, const float* gates,
                           int K, const int32_t* offsets, const int32_t* pairs, float* y, char* ws,
                           const PrefillWs& L, hipStream_t s);
-hipError_t launch_prefill_q8(const moe_experts_t& ex, const void* x, int x_bf16, int T, const float* gates,
-                             int K, const int32_t* offsets, const int32_t* pairs, float* y, char* ws,
-                             const PrefillQ8Ws& L, hipStream_t s);
-hipError_t launch_quantize_q8(const void* x, int x_bf16, size_t nblocks, int8_t* q, float* d, hipStream_t s);
-// pieces of the fp16 prefill shared with the int8 one
-hipError_t launch_prefill_tiles(const int32_t* offsets, int E, int P, int max_tiles, int4* tiles, int* ntiles,
-                                hipStream_t s);
-hipError_t launch_prefill_combine(const float* obuf, int T, int K, int D, float* y, hipStream_t s);
 hipError_t launch_decode_stack(const moe_stack_t& m, const void* x, int x_bf16, int T, float* h_out,
                                int32_t* ids_out, float* gates_out, float* h_layers, double eps, char* ws,
                                const StackWs& L, int G, hipStream_t s);

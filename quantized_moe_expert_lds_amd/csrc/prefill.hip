@@ -26,7 +26,7 @@
 // Workgroups map to tiles so that the 8 XCDs take interleaved m-tiles and
 // each XCD sweeps all column tiles of an m-tile back to back (the gathered
 // activation rows stay in that XCD's L2).
-#include "common.hpp"
+#include "prefill_q8.hpp"
 
 namespace {
 

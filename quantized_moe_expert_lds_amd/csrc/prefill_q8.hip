@@ -28,7 +28,7 @@
 // fused multiply-add); at 16 lanes per clock per SIMD against ~1,000 int8
 // multiply-adds, the block scaling and not the matrix core bounds these
 // kernels.
-#include "common.hpp"
+#include "prefill_q8.hpp"
 
 namespace {
 
