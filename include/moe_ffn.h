@@ -268,15 +268,16 @@ size_t moe_stack_workspace_size(const moe_stack_t* model, int n_tokens);
  * ~22 significant bits, with fp32 accumulation).  Results for a token do not
  * depend on n_tokens or on the other tokens (bitwise).
  *
- * Runs as one cooperative launch with one workgroup per compute unit that
- * stays resident for all layers; the workgroups hand logits, residual rows
- * and SwiGLU rows to each other through the workspace, tagged with per-token-
+ * Runs as one launch with one workgroup per compute unit that stays
+ * resident for all layers; the workgroups hand logits, residual rows and
+ * SwiGLU rows to each other through the workspace, tagged with per-token-
  * slot epochs kept in its header (a workspace can serve any sequence of
- * launches and batch sizes).  If the workgroups cannot all be resident the
- * launch fails with MOE_ERR_HIP; should a wait nevertheless last longer than
- * a few seconds, the kernel stops, the int at byte offset
- * MOE_STACK_ERROR_OFFSET of ws becomes nonzero, the outputs are undefined and
- * ws must be zero-filled again before reuse.
+ * launches and batch sizes).  If a compute unit cannot hold a workgroup the
+ * call fails with MOE_ERR_HIP.  The workgroups must run at the same time:
+ * should other work keep compute units busy, or should a wait last longer
+ * than a few seconds for any other reason, the kernel stops, the int at byte
+ * offset MOE_STACK_ERROR_OFFSET of ws becomes nonzero, the outputs are
+ * undefined and ws must be zero-filled again before reuse.
  *
  *   x            device [n_tokens][d_model], fp32 or bf16 (|x| < 65504)
  *   h_out        device fp32 [n_tokens][d_model] (output)

@@ -1219,11 +1219,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     }
 }
 
+// A plain launch of G <= (compute units) workgroups, which must all be
+// resident at once (they wait for each other's words).  A compute unit holds
+// one: checked once per device with the occupancy API at the largest
+// dynamic LDS size, and the LDS plan never asks for more.  A cooperative
+// launch would guarantee residency too, but its dispatch costs more than
+// several layers of this kernel (measured).  Should other work hold compute
+// units for longer than the kernel's wall-clock limit, the waits end there
+// with the error word set.
 template <int T, int BITS, int KPER, int EPWM>
 hipError_t launch_stack_t(StackParams& P, size_t lds, hipStream_t s) {
     auto fn = decode_stack_kernel<T, BITS, KPER, EPWM>;
-    // the dynamic LDS limit is raised once per device; two threads making
-    // their first call at the same time both set the same value
+    // the dynamic LDS limit is raised and residency checked once per device;
+    // two threads making their first call at the same time do the same work
     static std::atomic<int> attr_done[kMaxDevices];
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
@@ -1234,13 +1242,17 @@ hipError_t launch_stack_t(StackParams& P, size_t lds, hipStream_t s) {
         hipFuncAttributes fa{};
         e = hipFuncGetAttributes(&fa, (const void*)fn);
         if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(kStackLdsLimit - fa.sharedSizeBytes));
+        const size_t dyn_max = kStackLdsLimit - fa.sharedSizeBytes;
+        e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max);
         if (e != hipSuccess) return e;
+        int per_cu = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, kThreads, dyn_max);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
         attr_done[dev].store(1, std::memory_order_release);
     }
     void* args[] = {&P};
-    return hipLaunchCooperativeKernel((const void*)fn, dim3(P.G), dim3(kThreads), args, (unsigned)lds, s);
+    return hipLaunchKernel((const void*)fn, dim3(P.G), dim3(kThreads), args, (unsigned)lds, s);
 }
 
 template <int T, int BITS>
