@@ -29,7 +29,7 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ workspace map
 struct RouteWs {
-    size_t zfull, hist, rank, total;
+    size_t zfull, hist, rank, counter, total;
 };
 struct DecodeWs {
     size_t h, total;
@@ -58,6 +58,8 @@ inline RouteWs route_ws_layout(int T, int D, int E, int K) {
     off += align256(sizeof(int) * nb * E);
     w.rank = off;
     off += align256(sizeof(int) * P);
+    w.counter = off;                     // small-batch router: workgroups done (zero between calls)
+    off += 256;
     w.total = off;
     return w;
 }

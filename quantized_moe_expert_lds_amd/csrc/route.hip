@@ -7,19 +7,20 @@
 // library's own design for gfx950.
 //
 // Two paths:
-//  * small batches (T <= 8, decode and verify): reading the router matrix is
-//    the whole cost.  The router is stored expert-major ([E][d_model]), so
-//    each workgroup reads the contiguous rows of two experts (16 KB) with
-//    128-bit loads and produces complete logits; a second small kernel (one
-//    wavefront per token) selects the top-k.  No cross-workgroup
-//    synchronisation inside a kernel.
+//  * small batches (T <= 8, decode and verify): one launch.  Reading the
+//    router matrix is the whole cost of the logits.  The router is stored
+//    expert-major ([E][d_model]), so each workgroup reads the contiguous rows
+//    of two experts (16 KB) with 128-bit loads and produces complete logits;
+//    the last workgroup to finish (a counter in the workspace) selects the
+//    top-k of every token, one wavefront per token, with the selections of
+//    the decode-step kernel.
 //  * large batches (prefill): an fp64 GEMM on the matrix cores
 //    (v_mfma_f64_16x16x4_f64) in which every logit is accumulated over d in
 //    ascending order, one fused multiply-add per d (each fp32 x fp32 product
 //    is exact in fp64, so this is the same rounding sequence as the plain
 //    definition; a GPU test checks the logits bit for bit), then one
 //    wavefront per token selects the top-k.
-#include "common.hpp"
+#include "wave_ops.hpp"
 
 #include <math.h>
 
@@ -38,9 +39,17 @@ __device__ __forceinline__ double load_x(const void* x, int x_bf16, size_t i) {
 // 2w and 2w+1 for every token.  Wave v covers expert 2w + (v & 1) and half
 // (v >> 1) of the d range; lane l owns 16 consecutive d of that half (an
 // expert row is contiguous in the expert-major router layout).
-template <int T>
-__global__ __launch_bounds__(256) void route_logits_kernel(moe_router_t r, const void* __restrict__ x, int x_bf16,
-                                                           double* __restrict__ z) {
+//
+// Then the workgroups count themselves out on a counter in the workspace
+// (the pattern of a fence by every writer, a barrier and one atomic add per
+// workgroup); the one that brings it to the grid size has every logit in
+// view after its own fence, selects the top-k of each token (wave v takes
+// tokens v, v + 4: the histogram selection, or the round-by-round one when
+// it declines) and resets the counter to zero for the next call.
+template <int T, int KPER>
+__global__ __launch_bounds__(256) void route_small_kernel(moe_router_t r, const void* __restrict__ x, int x_bf16,
+                                                          double* __restrict__ z, unsigned* __restrict__ counter,
+                                                          int32_t* __restrict__ ids, float* __restrict__ gates) {
     const int E = r.n_experts, D = r.d_model;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = blockIdx.x * 2 + (wave & 1);
@@ -84,7 +93,32 @@ __global__ __launch_bounds__(256) void route_logits_kernel(moe_router_t r, const
             if (r.bias) s += (double)r.bias[ee];
             z[(size_t)t * E + ee] = s;
         }
+        __threadfence();
     }
+    __shared__ int s_last;
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    // the last workgroup: the selections, reading the logits from memory
+    const int K = r.top_k;
+    __shared__ double s_cv[4][128];
+    __shared__ int s_ci[4][128];
+    __shared__ unsigned s_ck[4][64];
+    __shared__ int s_hist[4][128];
+    __shared__ double s_sv[4][64];
+    __shared__ int s_si[4][64];
+    for (int t = wave; t < T; t += 4) {
+        const double* zt = z + (size_t)t * E;
+        if (!wave_topk_hist<KPER>(zt, E, K, s_sv[wave], s_si[wave], s_hist[wave], s_cv[wave], s_ci[wave]))
+            wave_topk_core<KPER>(zt, 0, E, K, s_sv[wave], s_si[wave], s_ck[wave]);
+        __builtin_amdgcn_wave_barrier();
+        wave_gates(s_sv[wave], s_si[wave], K, ids + (size_t)t * K, gates + (size_t)t * K);
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (tid == 0) *counter = 0u;
 }
 
 // ---------------------------------------------------------------- large T
@@ -205,22 +239,31 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ z,
 
 namespace qmoe {
 
-hipError_t launch_route_small(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
-                              float* gates, char* ws, const RouteWs& L, hipStream_t s) {
-    double* z = (double*)(ws + L.zfull);
+template <int KPER>
+hipError_t launch_route_small_k(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
+                                float* gates, double* z, unsigned* counter, hipStream_t s) {
     const unsigned grid = (unsigned)cdiv(r.n_experts, 2);
     switch (T) {
-#define QMOE_CASE(N)                                                         \
-    case N:                                                                  \
-        route_logits_kernel<N><<<grid, 256, 0, s>>>(r, x, x_bf16, z); \
+#define QMOE_CASE(N)                                                                                  \
+    case N:                                                                                           \
+        route_small_kernel<N, KPER><<<grid, 256, 0, s>>>(r, x, x_bf16, z, counter, ids, gates); \
         break;
         QMOE_CASE(1) QMOE_CASE(2) QMOE_CASE(3) QMOE_CASE(4) QMOE_CASE(5) QMOE_CASE(6) QMOE_CASE(7) QMOE_CASE(8)
 #undef QMOE_CASE
         default:
             return hipErrorInvalidValue;
     }
-    topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(z, T, r.n_experts, r.top_k, ids, gates);
     return hipGetLastError();
+}
+
+hipError_t launch_route_small(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
+                              float* gates, char* ws, const RouteWs& L, hipStream_t s) {
+    double* z = (double*)(ws + L.zfull);
+    unsigned* counter = (unsigned*)(ws + L.counter);
+    // logits per lane in the selections: a compile-time bound on n_experts
+    if (r.n_experts <= 128) return launch_route_small_k<2>(r, x, x_bf16, T, ids, gates, z, counter, s);
+    if (r.n_experts <= 512) return launch_route_small_k<8>(r, x, x_bf16, T, ids, gates, z, counter, s);
+    return launch_route_small_k<16>(r, x, x_bf16, T, ids, gates, z, counter, s);
 }
 
 hipError_t launch_route_large(const moe_router_t& r, const void* x, int x_bf16, int T, int32_t* ids,
