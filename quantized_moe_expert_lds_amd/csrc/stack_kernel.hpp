@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
     const moe_stack_t& m = P.m;
     const int L = m.n_layers, E = m.n_experts, D = m.d_model, F = m.d_ff, K = m.top_k;
     const int G = P.G, w = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const UnpackConsts uk = make_unpack_consts<BITS>();
     const int nkbD = D >> 5, nkbF = F >> 5, nch = F >> 4;
     const int PT = T * K;
@@ -373,6 +373,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             x_ = opaque_ptr(x_);
             asm volatile("" : "+v"(tid_));
         }
+        // the thread's indices inside the layer derive from the opaque copy
+        const int tid = tid_, lane = tid_ & 63, wave = tid_ >> 6;
         // ------------------------------------------------------------- ROUTE
         float bias_v = 0.0f;           // bias of (expert j, token t) for thread j*T + t
         if (m.router_b && tid < EPWM * T) {
