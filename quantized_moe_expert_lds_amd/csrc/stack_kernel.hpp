@@ -796,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             }
             STACK_CHECK_OK(ok);
             const uint32_t* hpp = P.hp + (size_t)l * hp_layer;
-            constexpr int kTG = T <= 2 ? T : 2;     // tokens whose h halves are held at once
+            constexpr int kTG = T <= 4 ? T : 2;     // tokens whose h halves are held at once
             for (int it = tid; it < U * nkbF; it += kThreads) {
                 const int u = it / nkbF, kb = it - u * nkbF;
                 const int e = s_uniq[u];
