@@ -449,15 +449,7 @@ def run(args, q, torch):
     del built
     torch.cuda.empty_cache()
     if not args.no_also:
-        log("single-layer decode with a MALL flush")
-        also["decode_1layer"] = bench_decode_1layer(q, torch)
-        torch.cuda.empty_cache()
-        log("prefill 8192")
-        also["prefill"] = bench_prefill(q, torch)
-        torch.cuda.empty_cache()
-        log("prefill 8192, int8 activations")
-        also["prefill_int8"] = bench_prefill(q, torch, int8=True)
-        torch.cuda.empty_cache()
+        # the other multi-layer steps come first, on freshly allocated stacks
         log("verify 4 tokens 3-bit")
         wv = mi.WORKLOADS["verify4_3bit"]
         bv = build_stack(q, torch, wv)
@@ -471,6 +463,15 @@ def run(args, q, torch):
         r = bench_stack(q, torch, wc, 100, 10, bc)
         also["experts256"] = stack_line("coder_256", wc.n_tokens, wc.n_layers, wc.n_experts, 2, *r)
         del bc
+        torch.cuda.empty_cache()
+        log("single-layer decode with a MALL flush")
+        also["decode_1layer"] = bench_decode_1layer(q, torch)
+        torch.cuda.empty_cache()
+        log("prefill 8192")
+        also["prefill"] = bench_prefill(q, torch)
+        torch.cuda.empty_cache()
+        log("prefill 8192, int8 activations")
+        also["prefill_int8"] = bench_prefill(q, torch, int8=True)
         torch.cuda.empty_cache()
 
     cpu = None
