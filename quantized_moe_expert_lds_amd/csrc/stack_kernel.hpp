@@ -596,11 +596,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         } else if (PT <= 64) {
             if (wave == 0) {
                 // lane p holds pair p; its expert's first pair is the lowest q
-                // with the same id; first pairs are numbered by a ballot
+                // with the same id, found by an atomic minimum in a table over
+                // the experts (the logits' LDS area, free after the top-k;
+                // the wave's LDS operations run in order); first pairs are
+                // numbered by a ballot
+                int* first_of = reinterpret_cast<int*>(s_z);
                 const int e = lane < PT ? s_ids[lane] : -1;
-                int firstq = lane;
-                for (int q = PT - 1; q >= 0; --q)
-                    if (__builtin_amdgcn_readlane(e, q) == e) firstq = q;
+                if (lane < PT) first_of[e] = 0x7fffffff;
+                if (lane < PT) atomicMin(&first_of[e], lane);
+                const int firstq = lane < PT ? first_of[e] : lane;
                 const bool first = lane < PT && firstq == lane;
                 const unsigned long long fm = __ballot(first);
                 const int idx = __popcll(fm & ((1ull << lane) - 1ull));
