@@ -231,6 +231,9 @@ __device__ __forceinline__ void gemm_kloop(const uint16_t* const* a_src, const u
             for (int i = 0; i < 4; ++i) a[i] = lds_frag(&As[64 * wm + 16 * i + (lane & 15)][kofs]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) b[j] = lds_frag(&Bs[128 * wn + 16 * j + (lane & 15)][kofs]);
+            // the matrix-core block runs at raised wave priority, so the other
+            // workgroup on the CU issues its dequant and LDS work meanwhile
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (!kFull && i >= ni) continue;            // slice beyond the bucket
@@ -238,6 +241,7 @@ __device__ __forceinline__ void gemm_kloop(const uint16_t* const* a_src, const u
                 for (int j = 0; j < 8; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
     }

@@ -204,6 +204,9 @@ __device__ __forceinline__ void q8_kloop(const Q8Src& src, int b_lds_row, int ns
                 b[j] = *reinterpret_cast<const long*>(&Bs[128 * wn + 16 * j + (lane & 15)][kofs]);
                 sb[j] = SB[kk][128 * wn + 16 * j + (lane & 15)];
             }
+            // products and their scaling at raised wave priority, as in the
+            // fp16 GEMMs
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (!kFull && i >= ni) continue;            // slice beyond the bucket
@@ -215,6 +218,7 @@ __device__ __forceinline__ void q8_kloop(const Q8Src& src, int b_lds_row, int ns
                         acc[i][j][v] = __builtin_fmaf((float)r[v], sa[i][v] * sb[j], acc[i][j][v]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
     }
