@@ -428,8 +428,8 @@ def run(args, q, torch):
         profile_pass(q, torch)
         return
     if args.prefill_pass:
-        print(json.dumps(bench_prefill(q, torch, steps=3, warmup=1)), flush=True)
-        print(json.dumps(bench_prefill(q, torch, steps=3, warmup=1, int8=True)), flush=True)
+        print(json.dumps(bench_prefill(q, torch, steps=10, warmup=2)), flush=True)
+        print(json.dumps(bench_prefill(q, torch, steps=10, warmup=2, int8=True)), flush=True)
         return
     wl = mi.WORKLOADS["decode_48layer"]
     log("48-layer decode, batch 1: generating 48 x 512 experts in HBM and timing")
@@ -521,7 +521,7 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="only 3 decode steps and a calibration copy, for rocprofv3 counter passes")
     ap.add_argument("--prefill-pass", action="store_true",
-                    help="only the 8,192-token prefill chunk (3 timed calls), for rocprofv3 passes")
+                    help="only the 8,192-token prefill chunk (10 timed calls per path), for rocprofv3 passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE FFN path is built and measured on a single MI355X "
