@@ -644,6 +644,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
         }
         lds_barrier();
         const int U = s_misc[0];
+        // For five or more tokens an item's cost grows with the number of
+        // tokens that chose its expert, so the items are dealt by weight: the
+        // distinct experts ranked by that number (descending, ties to the
+        // lower index; s_order[rank] = distinct index), their chunks in rank
+        // order, one pass over the workgroups forward, the next backward.
+        // Which workgroup computes an item does not change its arithmetic.
+        // (At 2-4 tokens the extra registers cost more than the balance gains.)
+        constexpr bool kBal = T >= 5;
+        int* s_order = s_first;
+        if constexpr (kBal) {
+            if (tid < U) {
+                int n = 0;
+#pragma unroll
+                for (int t = 0; t < T; ++t) n += s_upair[tid * T + t] >= 0;
+                int rank = 0;
+                for (int v = 0; v < U; ++v) {
+                    int nv = 0;
+#pragma unroll
+                    for (int t = 0; t < T; ++t) nv += s_upair[v * T + t] >= 0;
+                    rank += nv > n || (nv == n && v < tid);
+                }
+                s_order[rank] = tid;
+            }
+            lds_barrier();
+        }
 
         const size_t lstrideD = (size_t)E * D * nkbF;
         // The down rows of this thread's first (expert, block) item, which
@@ -672,15 +697,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
             const size_t lstrideGU = (size_t)E * F * nkbD;
             const bool kact = lane < nkbD;                    // d_model <= 2048: one block per lane
             const int kbc = kact ? lane : nkbD - 1;           // loads stay in bounds
+            // item a of the round starting at it0 (pass (it0 - w) / G + a): w,
+            // or G - 1 - w on odd passes of the weighted order; valid below
+            // n_items
+            auto ita = [&](int it0, int a) {
+                if constexpr (kBal) {
+                    const int p = (it0 - w) / G + a;
+                    return p * G + ((p & 1) ? G - 1 - w : w);
+                }
+                return it0 + a * G;
+            };
+            // distinct expert of item it: by rank when dealt by weight
+            auto item_expert = [&](int it) { return kBal ? s_order[it / nch] : it / nch; };
             for (int it0 = w; it0 < n_items; it0 += G * kMaxItemsInFlight) {
                 int tmask[kMaxItemsInFlight];       // tokens that chose the item's expert
                 int ie[kMaxItemsInFlight];          // the item's expert
 #pragma unroll
                 for (int a = 0; a < kMaxItemsInFlight; ++a) {
-                    const int it = it0 + a * G;
+                    const int it = ita(it0, a);
                     int msk = 0, e = 0;
                     if (it < n_items) {
-                        const int u = it / nch;
+                        const int u = item_expert(it);
 #pragma unroll
                         for (int t = 0; t < T; ++t) msk |= (s_upair[u * T + t] >= 0) << t;
                         e = s_uniq[u];
@@ -692,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                 uint16_t sr[kMaxItemsInFlight][8];
 #pragma unroll
                 for (int a = 0; a < kMaxItemsInFlight; ++a) {
-                    const int it = it0 + a * G;
+                    const int it = ita(it0, a);
                     if (it >= n_items) continue;
                     const int c = it - (it / nch) * nch;
                     const int f0 = 16 * c + 4 * wave;
@@ -723,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         bool any = false;
 #pragma unroll
                         for (int a = 0; a < kMaxItemsInFlight; ++a)
-                            any = any || (it0 + a * G < n_items && ((tmask[a] >> t) & 1));
+                            any = any || (ita(it0, a) < n_items && ((tmask[a] >> t) & 1));
                         if (!any) continue;
                         uint32_t xt[32];
 #pragma unroll
@@ -736,7 +773,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         }
 #pragma unroll
                         for (int a = 0; a < kMaxItemsInFlight; ++a) {
-                            if (it0 + a * G >= n_items || !((tmask[a] >> t) & 1)) continue;
+                            if (ita(it0, a) >= n_items || !((tmask[a] >> t) & 1)) continue;
 #pragma unroll
                             for (int r = 0; r < 8; ++r) {
                                 uint32_t lv[16];
@@ -748,7 +785,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                         }
                     }
                     const int a = lane / (4 * T), t = (lane >> 2) % T, r = lane & 3;
-                    if (a < kMaxItemsInFlight && it0 + a * G < n_items && ((tmask[a] >> t) & 1)) {
+                    bool take;
+                    if constexpr (kBal) {
+                        int tm = 0;                 // tokens of this lane's item (none past the last)
+#pragma unroll
+                        for (int b = 0; b < kMaxItemsInFlight; ++b)
+                            if (a == b && ita(it0, b) < n_items) tm = tmask[b];
+                        take = a < kMaxItemsInFlight && ((tm >> t) & 1);
+                    } else {
+                        take = a < kMaxItemsInFlight && it0 + a * G < n_items && ((tmask[a] >> t) & 1);
+                    }
+                    if (take) {
                         gv = gu[(a * T + t) * 8 + r];
                         uv = gu[(a * T + t) * 8 + 4 + r];
                     }
@@ -758,16 +805,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_stack_kernel(StackParams P
                     int tm = 0;
 #pragma unroll
                     for (int b = 0; b < kMaxItemsInFlight; ++b)
-                        if (a == b && it0 + b * G < n_items) tm = tmask[b];
+                        if (a == b && ita(it0, b) < n_items) tm = tmask[b];
                     const float hv = silu_mul(gv, uv);
                     if (a < kMaxItemsInFlight && ((tm >> t) & 1)) s_hloc[(a * T + t) * 16 + 4 * wave + r] = hv;
                 }
                 lds_barrier();
                 if (tid < 8 * T * kMaxItemsInFlight) {
                     const int a = tid / (8 * T), rem = tid - a * 8 * T, t = rem >> 3, mm = rem & 7;
-                    const int it = it0 + a * G;
+                    const int it = ita(it0, a);
                     if (it < n_items) {
-                        const int u = it / nch, c = it - u * nch;
+                        const int u = item_expert(it), c = it - (kBal ? it / nch : u) * nch;
                         const int pr = s_upair[u * T + t];
                         if (pr >= 0) {
                             _Float16 h0, l0, h1, l1;
