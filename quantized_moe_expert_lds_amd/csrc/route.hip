@@ -123,30 +123,34 @@ __global__ __launch_bounds__(256) void route_small_kernel(moe_router_t r, const 
 
 // ---------------------------------------------------------------- large T
 // fp64 matrix cores (v_mfma_f64_16x16x4_f64).  A block of 256 threads
-// computes a 128-token x 64-expert tile of z; d runs in chunks of 32 through
+// computes a 64-token x 64-expert tile of z; d runs in chunks of 32 through
 // LDS, where x and w sit as fp64, transposed ([d][token], [d][expert]) so a
 // fragment read is 16 consecutive doubles.  Wave v owns tokens
-// 64 (v & 1) .. +64 and experts 32 (v >> 1) .. +32: 4 x 2 MFMA tiles, each
+// 32 (v & 1) .. +32 and experts 32 (v >> 1) .. +32: 2 x 2 MFMA tiles, each
 // accumulating over d in ascending groups of 4.  The next chunk is loaded
-// into registers while the current one multiplies.
+// into registers while the current one multiplies.  An 8,192-token chunk
+// over 512 experts gives 1,024 blocks, four per CU (four waves per SIMD to
+// cover the barriers and loads); 128-token tiles (two per CU) took ~30 us
+// more per chunk, 32-token tiles ~15 us more.
 typedef double double4_t __attribute__((ext_vector_type(4)));
-constexpr int kR64T = 128, kR64E = 64, kR64K = 32;
+constexpr int kR64T = 64, kR64E = 64, kR64K = 32;
 
-__global__ __launch_bounds__(256, 2) void route_gemm_kernel(moe_router_t r, const void* __restrict__ x,
+__global__ __launch_bounds__(256, 4) void route_gemm_kernel(moe_router_t r, const void* __restrict__ x,
                                                             int x_bf16, int T, double* __restrict__ z) {
     const int E = r.n_experts, D = r.d_model;
     const int e0 = blockIdx.x * kR64E, t0 = blockIdx.y * kR64T;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wt = 64 * (wave & 1), we = 32 * (wave >> 1);
+    constexpr int kTI = kR64T / 32, kXL = kR64T * kR64K / 4 / 256;   // token tiles per wave, x loads per thread
+    const int wt = (kR64T / 2) * (wave & 1), we = 32 * (wave >> 1);
     __shared__ double xs[kR64K][kR64T + 1];
     __shared__ double ws_[kR64K][kR64E + 1];
 
     // staging: float4 f = tid + 256 i of a chunk holds d 4 (f & 7) .. +3 of
     // token (or expert) f >> 3
-    float4 xr[4], wr[2];
+    float4 xr[kXL], wr[2];
     auto load = [&](int d0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kXL; ++i) {
             const int f = tid + 256 * i, t = t0 + (f >> 3), d = d0 + 4 * (f & 7);
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (t < T) {
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(moe_router_t r, cons
     };
     auto store = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kXL; ++i) {
             const int f = tid + 256 * i, t = f >> 3, dd = 4 * (f & 7);
             xs[dd][t] = xr[i].x;
             xs[dd + 1][t] = xr[i].y;
@@ -186,9 +190,9 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(moe_router_t r, cons
         }
     };
 
-    double4_t acc[4][2];
+    double4_t acc[kTI][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = double4_t{0.0, 0.0, 0.0, 0.0};
     load(0);
@@ -199,13 +203,13 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(moe_router_t r, cons
 #pragma unroll
         for (int kk = 0; kk < kR64K / 4; ++kk) {
             const int k = 4 * kk + (lane >> 4);
-            double a[4], b[2];
+            double a[kTI], b[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[k][wt + 16 * i + (lane & 15)];
+            for (int i = 0; i < kTI; ++i) a[i] = xs[k][wt + 16 * i + (lane & 15)];
 #pragma unroll
             for (int j = 0; j < 2; ++j) b[j] = ws_[k][we + 16 * j + (lane & 15)];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kTI; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(moe_router_t r, cons
         if (e >= E) continue;
         const double bias = r.bias ? (double)r.bias[e] : 0.0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kTI; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int t = t0 + wt + 16 * i + (lane >> 4) + 4 * v;
