@@ -380,6 +380,37 @@ def test_route_logits_bit_exact_8192(q, full1):
     assert np.array_equal(z[sample], z_o), f"{np.mean(z[sample] != z_o):.3f} of the sampled logits differ"
 
 
+@pytest.mark.parametrize("T", [9, 63, 64, 65, 129])
+def test_route_gemm_tile_boundaries(q, full1, T):
+    """The matrix-core router GEMM works on 64-token x 64-expert tiles: token
+    counts just below, at and above a tile edge (and 9, the smallest count
+    that takes this path) give the oracle's ids, gates and buckets, and every
+    fp64 logit of every token bit for bit, for bf16 and fp32 activations."""
+    _say(f"moe_route T={T}: 64-token router GEMM tiles, bf16 and fp32 inputs")
+    wl = mi.WORKLOADS["prefill_8192"]
+    _, layers, _, _ = full1
+    router, _ = layers[0]
+    K, E, D = wl.top_k, wl.n_experts, wl.d_model
+    wh, bh = mi.router_host(wl, 0)
+    xb = mi.activations_host(wl, T)
+    xf = xb.astype(np.uint32) << 16
+    xf = xf.view(np.float32)                   # the same values as fp32
+    for x_host, x_dev in ((xb, torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)),
+                          (xf, torch.from_numpy(np.ascontiguousarray(xf)).cuda())):
+        ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        prs = torch.empty(T * K, dtype=torch.int32, device="cuda")
+        ws = q.workspace(q.MOE_OP_ROUTE, T, D, 0, E, K)
+        q.moe_route(router, x_dev, ids, w, off, prs, ws)
+        torch.cuda.synchronize()
+        z = ws[: T * E * 8].view(torch.float64).reshape(T, E).cpu().numpy()
+        z_o = O.router_logits(x_host, wh, bh)
+        assert np.array_equal(z, z_o), f"{np.mean(z != z_o):.4f} of the logits differ"
+        ids_o, gates_o, _ = O.route(x_host, wh, bh, K)
+        check_routing(ids, w, off, prs, ids_o, gates_o, E)
+
+
 # ------------------------------------------------------------- errors
 
 def test_abi_errors(q, tiny):
