@@ -411,6 +411,29 @@ def test_route_gemm_tile_boundaries(q, full1, T):
         check_routing(ids, w, off, prs, ids_o, gates_o, E)
 
 
+@pytest.mark.parametrize("E", [16, 100, 200])
+def test_route_gemm_ragged_experts(q, E):
+    """The router GEMM's last 64-expert tile partly empty (and a bias): 70
+    tokens (two token tiles, the second ragged) on seeded random routers whose
+    expert count is not a multiple of 64; logits bit for bit, ids, gates and
+    buckets against the oracle."""
+    _say(f"moe_route T=70 E={E}: ragged expert tiles of the router GEMM, with bias")
+    rng = np.random.default_rng(1000 + E)
+    D, T, K = 256, 70, min(8, E)
+    w = (0.02 * rng.standard_normal((D, E))).astype(np.float32)
+    b = (0.01 * rng.standard_normal(E)).astype(np.float32)
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    router = q.Router(torch.from_numpy(np.ascontiguousarray(w.T)).cuda(), torch.from_numpy(b).cuda(), K)
+    ids, g, off, prs = gpu_route(q, router, torch.from_numpy(x).cuda())
+    ws = q.workspace(q.MOE_OP_ROUTE, T, D, 0, E, K)
+    q.moe_route(router, torch.from_numpy(x).cuda(), torch.empty_like(ids), torch.empty_like(g), None, None, ws)
+    torch.cuda.synchronize()
+    z = ws[: T * E * 8].view(torch.float64).reshape(T, E).cpu().numpy()
+    assert np.array_equal(z, O.router_logits(x, w, b)), "router logits differ"
+    ids_o, gates_o, _ = O.route(x, w, b, K)
+    check_routing(ids, g, off, prs, ids_o, gates_o, E)
+
+
 # ------------------------------------------------------------- errors
 
 def test_abi_errors(q, tiny):
